@@ -1,0 +1,151 @@
+"""fp64 CPU reference for exact softmax attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only callers.  The GPU package never
+imports this module, and this module imports nothing from the GPU package.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, materialises the
+score matrix per head); this wrapper only marshals numpy arrays.  What it
+computes, with citations, is stated at the top of that file:
+
+    S = scale * Q K^T (masked entries -inf), P = softmax(S) row-wise,
+    O = P V, LSE = m + ln(l)
+
+All functions pinned by tests/test_oracle_pins.py (brute force at 50 digits,
+torch float64 SDPA, closed forms and invariants); no function here is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "attn_oracle.c")
+LIBRARY = os.path.join(HERE, "libattn_oracle.so")
+
+KINDS = {"f16": 1, "bf16": 2}
+
+
+def build(source: str = SOURCE, out: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the reference with gcc (-O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", *extra_flags,
+           source, "-lm", "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_i64 = ctypes.c_int64
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def _ptr(a: np.ndarray, ctype=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class Oracle:
+    """ctypes handle on one build of attn_oracle.c."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            build(out=path)
+        lib = ctypes.CDLL(path)
+        lib.fa_oracle_widen.argtypes = [ctypes.POINTER(ctypes.c_uint16), _dp, _i64, ctypes.c_int]
+        lib.fa_oracle_widen.restype = ctypes.c_int
+        lib.fa_oracle_attention.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64,
+                                            ctypes.c_int, ctypes.c_double]
+        lib.fa_oracle_attention.restype = ctypes.c_int
+        lib.fa_oracle_attention_rows.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int,
+                                                 ctypes.c_double, ctypes.POINTER(_i64), _i64,
+                                                 _dp, _dp]
+        lib.fa_oracle_attention_rows.restype = ctypes.c_int
+        lib.fa_oracle_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    # -- inputs -----------------------------------------------------------
+    def widen(self, bits: np.ndarray, dtype: str) -> np.ndarray:
+        """Exact float64 values of uint16 bit patterns of type dtype ('f16' or 'bf16')."""
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, dtype=np.float64)
+        rc = self.lib.fa_oracle_widen(_ptr(bits, ctypes.c_uint16), _ptr(out), bits.size,
+                                      KINDS[dtype])
+        if rc:
+            raise ValueError("widen failed")
+        return out
+
+    def _as_f64(self, x: np.ndarray, dtype):
+        if dtype is None:
+            return np.ascontiguousarray(x, dtype=np.float64)
+        return self.widen(x, dtype)
+
+    # -- attention --------------------------------------------------------
+    def attention(self, q, k, v, *, causal: bool, scale: float, dtype=None):
+        """O [B,H,Nq,d] and LSE [B,H,Nq] in float64.
+
+        q, k, v are [B,H,N,d] (or [N,d] for a single head) float arrays, or
+        uint16 bit patterns when dtype is 'f16'/'bf16'."""
+        q, k, v = (self._as_f64(t, dtype) for t in (q, k, v))
+        squeeze = q.ndim == 2
+        if squeeze:
+            q, k, v = q[None, None], k[None, None], v[None, None]
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
+            raise ValueError("shape mismatch")
+        o = np.empty((B, H, Nq, d), dtype=np.float64)
+        lse = np.empty((B, H, Nq), dtype=np.float64)
+        rc = self.lib.fa_oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq,
+                                          Nkv, d, int(bool(causal)), float(scale))
+        if rc:
+            raise ValueError(f"oracle rejected the call (rc={rc})")
+        if squeeze:
+            return o[0, 0], lse[0, 0]
+        return o, lse
+
+    def attention_rows(self, q, k, v, rows, *, causal: bool, scale: float, dtype=None):
+        """Selected query rows of one head: q [Nq,d], k/v [Nkv,d] -> O [n,d], LSE [n]."""
+        q, k, v = (self._as_f64(t, dtype) for t in (q, k, v))
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        Nq, d = q.shape
+        Nkv = k.shape[0]
+        o = np.empty((rows.size, d), dtype=np.float64)
+        lse = np.empty(rows.size, dtype=np.float64)
+        rc = self.lib.fa_oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), Nq, Nkv, d,
+                                               int(bool(causal)), float(scale),
+                                               _ptr(rows, _i64), rows.size, _ptr(o), _ptr(lse))
+        if rc:
+            raise ValueError(f"oracle rejected the call (rc={rc})")
+        return o, lse
+
+    def threads(self) -> int:
+        return int(self.lib.fa_oracle_threads())
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def widen(bits, dtype):
+    return default().widen(bits, dtype)
+
+
+def attention(q, k, v, *, causal, scale, dtype=None):
+    return default().attention(q, k, v, causal=causal, scale=scale, dtype=dtype)
+
+
+def attention_rows(q, k, v, rows, *, causal, scale, dtype=None):
+    return default().attention_rows(q, k, v, rows, causal=causal, scale=scale, dtype=dtype)
+
+
+def threads() -> int:
+    return default().threads()

@@ -1,0 +1,232 @@
+/*
+ * attn_oracle.c -- plain, slow fp64 CPU reference for exact softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the package smoke check and the
+ * CPU-baseline leg of the benchmark are the only code that loads this library.
+ * The GPU library neither links nor includes anything from here, and nothing
+ * here comes from the GPU library.
+ *
+ * What it computes, for every batch b, head h and query row i:
+ *
+ *   S[i][j] = scale * sum_c q[i][c] * k[j][c]   for every key j visible to i,
+ *             -infinity                          for keys that are not visible.
+ *       Standard attention S = Q K^T, P = softmax(S), O = P V ("FlashAttention",
+ *       section "The problem: the n x n score matrix"), with the 1/sqrt(d)
+ *       factor of "Flash Attention -- Module 12.3", section "Definition",
+ *       generalised to a caller-supplied scale.
+ *
+ *   m_i     = max_j S[i][j]
+ *   l_i     = sum_j exp(S[i][j] - m_i)
+ *   P[i][j] = exp(S[i][j] - m_i) / l_i
+ *       The two-pass stable softmax of "FlashAttention 1-2-3: The IO-Aware
+ *       Revolution in LLM Inference", section "The Math Behind the Online
+ *       Softmax Trick" (find the max, exponentiate the shifted values, sum,
+ *       divide).
+ *
+ *   O[i][c] = sum_j P[i][j] * v[j][c]
+ *   LSE_i   = m_i + ln(l_i)
+ *       LSE is not named on the pages; it is the natural logarithm of
+ *       sum_j exp(S[i][j]), i.e. the row's (m, l) pair folded into one number.
+ *
+ * Causal visibility: key j is visible to row i iff j <= i + (Nkv - Nq).  With
+ * Nq == Nkv this is the lower triangle including the diagonal; for Nq < Nkv the
+ * last query row sees every key (the alignment is a reading: the pages show
+ * only square causal masks).  Causal with Nq > Nkv is rejected.
+ *
+ * Inputs are row-major [B][H][N][d] arrays of doubles; 16-bit inputs are first
+ * widened exactly by fa_oracle_widen.  For each head the full Nq x Nkv score
+ * matrix is materialised, softmaxed in place into P, and multiplied by V: the
+ * three passes of standard attention, nothing blocked, fused or reordered.
+ * Rows are spread over OpenMP threads; every row's arithmetic is sequential in
+ * key order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE 754 binary16: sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double fa_oracle_f16_to_f64(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int expo = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -24);              /* subnormal: frac * 2^-14 * 2^-10 */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x400), expo - 25); /* 1.frac * 2^(expo-15) */
+    return sign ? -mag : mag;
+}
+
+/* bfloat16: sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double fa_oracle_bf16_to_f64(uint16_t bits)
+{
+    int sign = bits >> 15;
+    int expo = (bits >> 7) & 0xff;
+    int frac = bits & 0x7f;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -133);             /* subnormal: frac * 2^-126 * 2^-7 */
+    else if (expo == 255)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(frac | 0x80), expo - 134); /* 1.frac * 2^(expo-127) */
+    return sign ? -mag : mag;
+}
+
+/* kind 1 = binary16, kind 2 = bfloat16.  Returns 0, or -1 for an unknown kind. */
+int fa_oracle_widen(const uint16_t *bits, double *out, int64_t n, int kind)
+{
+    if (kind != 1 && kind != 2)
+        return -1;
+    for (int64_t t = 0; t < n; ++t)
+        out[t] = kind == 1 ? fa_oracle_f16_to_f64(bits[t]) : fa_oracle_bf16_to_f64(bits[t]);
+    return 0;
+}
+
+int fa_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int is_visible(int64_t i, int64_t j, int64_t Nq, int64_t Nkv, int causal)
+{
+    return !causal || j <= i + (Nkv - Nq);
+}
+
+/* Row i of S: scaled dot products with every visible key, -inf elsewhere. */
+static void score_row(const double *qi, const double *k, int64_t i, int64_t Nq, int64_t Nkv,
+                      int64_t d, int causal, double scale, double *s_row)
+{
+    for (int64_t j = 0; j < Nkv; ++j) {
+        if (!is_visible(i, j, Nq, Nkv, causal)) {
+            s_row[j] = -INFINITY;
+            continue;
+        }
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += qi[c] * k[j * d + c];
+        s_row[j] = scale * dot;
+    }
+}
+
+/* Two-pass stable softmax of one row, in place (S row -> P row).  Returns LSE. */
+static double softmax_row(double *s_row, int64_t Nkv)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < Nkv; ++j)
+        if (s_row[j] > m)
+            m = s_row[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < Nkv; ++j) {
+        s_row[j] = exp(s_row[j] - m);
+        l += s_row[j];
+    }
+    for (int64_t j = 0; j < Nkv; ++j)
+        s_row[j] = s_row[j] / l;
+    return m + log(l);
+}
+
+/* Row i of O = P V (sum over keys in ascending order for every column). */
+static void pv_row(const double *p_row, const double *v, int64_t Nkv, int64_t d, double *oi)
+{
+    for (int64_t c = 0; c < d; ++c)
+        oi[c] = 0.0;
+    for (int64_t j = 0; j < Nkv; ++j) {
+        double p = p_row[j];
+        for (int64_t c = 0; c < d; ++c)
+            oi[c] += p * v[j * d + c];
+    }
+}
+
+static int check_shape(int64_t Nq, int64_t Nkv, int64_t d, int causal)
+{
+    if (Nq < 0 || Nkv < 1 || d < 1)
+        return -1;
+    if (causal && Nq > Nkv)
+        return -1;
+    return 0;
+}
+
+/* One head: S materialised (Nq x Nkv), then P in place, then O.  -2 if out of memory. */
+static int head_attention(const double *q, const double *k, const double *v, double *o,
+                          double *lse, int64_t Nq, int64_t Nkv, int64_t d, int causal,
+                          double scale)
+{
+    double *S = (double *)malloc((size_t)Nq * (size_t)Nkv * sizeof(double));
+    if (!S)
+        return -2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < Nq; ++i)
+        score_row(q + i * d, k, i, Nq, Nkv, d, causal, scale, S + i * Nkv);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < Nq; ++i)
+        lse[i] = softmax_row(S + i * Nkv, Nkv);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < Nq; ++i)
+        pv_row(S + i * Nkv, v, Nkv, d, o + i * d);
+    free(S);
+    return 0;
+}
+
+/*
+ * Full attention over [B][H][N][d] inputs.  o: [B][H][Nq][d], lse: [B][H][Nq].
+ * Returns 0, -1 for an invalid shape, -2 if the score matrix cannot be allocated.
+ */
+int fa_oracle_attention(const double *q, const double *k, const double *v, double *o, double *lse,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, int causal,
+                        double scale)
+{
+    if (B < 0 || H < 0 || check_shape(Nq, Nkv, d, causal))
+        return -1;
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int rc = head_attention(q + bh * Nq * d, k + bh * Nkv * d, v + bh * Nkv * d,
+                                o + bh * Nq * d, lse + bh * Nq, Nq, Nkv, d, causal, scale);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
+/*
+ * Selected rows of one head, for spot checks at sizes where a whole head's S is
+ * too large to hold: the same three passes on a one-row S.  q, k, v are one
+ * head ([Nq][d], [Nkv][d], [Nkv][d]); rows lists query indices; o gets
+ * [nrows][d], lse [nrows].
+ */
+int fa_oracle_attention_rows(const double *q, const double *k, const double *v, int64_t Nq,
+                             int64_t Nkv, int64_t d, int causal, double scale,
+                             const int64_t *rows, int64_t nrows, double *o, double *lse)
+{
+    if (check_shape(Nq, Nkv, d, causal))
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= Nq)
+            return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        double *s_row = (double *)malloc((size_t)Nkv * sizeof(double));
+        if (!s_row) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        int64_t i = rows[r];
+        score_row(q + i * d, k, i, Nq, Nkv, d, causal, scale, s_row);
+        lse[r] = softmax_row(s_row, Nkv);
+        pv_row(s_row, v, Nkv, d, o + r * d);
+        free(s_row);
+    }
+    return failed ? -2 : 0;
+}

@@ -1,0 +1,348 @@
+"""Checks that pin the fp64 attention reference to things other than itself.
+
+Every function takes an ``oracle.Oracle`` handle and raises AssertionError when
+the reference disagrees with the pin.  tests/test_oracle_pins.py runs them on
+the real build; tests/test_oracle_mutants.py runs them on builds with planted
+mistakes and requires each mistake to be caught.
+
+What the pins rest on:
+  * the definition softmax(scale * Q K^T) V evaluated independently: a
+    50-digit decimal brute force without the max shift, and torch's float64
+    scaled_dot_product_attention / logsumexp (library special cases);
+  * closed forms and invariants of the definition: constant V, Q = 0,
+    causal row 0, a dominant score, a single key, the worked two-key example,
+    convex-combination bounds, exact power-of-two linearity in V, joint
+    permutation of K and V, invariance under a uniform shift of the scores;
+  * the two-block merge of partial softmax results ("FlashAttention 1-2-3:
+    The IO-Aware Revolution in LLM Inference", section "The Math Behind the
+    Online Softmax Trick"): attention over all keys equals the merge of
+    attention over two disjoint key sets, for any split point;
+  * exact decoding of the 16-bit storage formats, against numpy (binary16)
+    and torch (bfloat16).
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, localcontext
+
+import numpy as np
+
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _visible_count(i, Nq, Nkv, causal):
+    return Nkv if not causal else min(Nkv, i + Nkv - Nq + 1)
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------------------
+# storage formats
+
+def pin_widen_f16(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.widen(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "f16 NaN patterns"
+    assert np.array_equal(got[~nan], ref[~nan]), "f16 decode differs from numpy"
+
+
+def pin_widen_bf16(orc):
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "bf16 NaN patterns"
+    assert np.array_equal(got[~nan], ref[~nan]), "bf16 decode differs from torch"
+    # a few closed forms: 1.0, -2.0, smallest subnormal, largest finite
+    assert orc.widen(np.array([0x3F80, 0xC000, 0x0001, 0x7F7F], np.uint16), "bf16").tolist() == [
+        1.0, -2.0, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127]
+
+
+# ---------------------------------------------------------------------------
+# independent evaluations of the definition
+
+def _decimal_attention(q, k, v, causal, scale):
+    """softmax(scale q k^T) v at 50 significant digits, straight from the definition."""
+    Nq, d = q.shape
+    Nkv = k.shape[0]
+    o = np.zeros((Nq, d))
+    lse = np.zeros(Nq)
+    with localcontext() as ctx:
+        ctx.prec = 50
+        sc = Decimal(scale)
+        for i in range(Nq):
+            weights = []
+            for j in range(Nkv):
+                if causal and j > i + (Nkv - Nq):
+                    continue
+                dot = sum(Decimal(float(q[i, c])) * Decimal(float(k[j, c])) for c in range(d))
+                weights.append((j, (sc * dot).exp()))
+            z = sum(w for _, w in weights)
+            for c in range(d):
+                num = sum(w * Decimal(float(v[j, c])) for j, w in weights)
+                o[i, c] = float(num / z)
+            lse[i] = float(z.ln())
+    return o, lse
+
+
+def pin_decimal_bruteforce(orc):
+    rng = _rng(11)
+    cases = [(1, 1, 1, False, 0.5), (5, 5, 3, True, 0.7), (4, 7, 4, True, 0.5),
+             (6, 6, 2, False, -0.9), (3, 8, 5, False, 0.45), (2, 2, 1, True, 1.0)]
+    for Nq, Nkv, d, causal, scale in cases:
+        q = rng.standard_normal((Nq, d))
+        k = rng.standard_normal((Nkv, d))
+        v = rng.standard_normal((Nkv, d))
+        o, lse = orc.attention(q, k, v, causal=causal, scale=scale)
+        o_ref, lse_ref = _decimal_attention(q, k, v, causal, scale)
+        _close(o, o_ref, what=f"O vs decimal {Nq}x{Nkv}x{d} causal={causal}")
+        _close(lse, lse_ref, what=f"LSE vs decimal {Nq}x{Nkv}x{d} causal={causal}")
+
+
+def pin_torch_sdpa(orc):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(12)
+    for B, H, Nq, Nkv, d, causal in [(2, 3, 17, 17, 8, True), (1, 2, 33, 64, 16, True),
+                                      (2, 1, 40, 23, 32, False), (1, 1, 64, 64, 64, True)]:
+        scale = 1.0 / math.sqrt(d)
+        q = rng.standard_normal((B, H, Nq, d))
+        k = rng.standard_normal((B, H, Nkv, d))
+        v = rng.standard_normal((B, H, Nkv, d))
+        o, lse = orc.attention(q, k, v, causal=causal, scale=scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        mask = torch.ones(Nq, Nkv, dtype=torch.bool)
+        if causal:
+            mask = mask.tril(diagonal=Nkv - Nq)
+        o_ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+        s = (tq @ tk.transpose(-1, -2)) * scale
+        lse_ref = torch.logsumexp(s.masked_fill(~mask, float("-inf")), dim=-1)
+        _close(o, o_ref.numpy(), what=f"O vs torch sdpa {B}x{H}x{Nq}x{Nkv}x{d}")
+        _close(lse, lse_ref.numpy(), what=f"LSE vs torch logsumexp {B}x{H}x{Nq}x{Nkv}x{d}")
+        if causal and Nq == Nkv:
+            o_ref2 = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+            _close(o, o_ref2.numpy(), what="O vs torch sdpa is_causal")
+
+
+# ---------------------------------------------------------------------------
+# closed forms and invariants
+
+def pin_two_key_worked(orc):
+    # scale 1, query (1, 0) against keys (0, 0) and (1, 0) -- scores 0 and 1 --
+    # with values e_0 and e_1: weights 1/(1+e) and e/(1+e), LSE ln(1+e).
+    q = np.array([[1.0, 0.0]])
+    k = np.array([[0.0, 0.0], [1.0, 0.0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0]])
+    o, lse = orc.attention(q, k, v, causal=False, scale=1.0)
+    e = math.e
+    _close(o, [[1 / (1 + e), e / (1 + e)]], 1e-15, "two-key weights")
+    _close(lse, [math.log1p(e)], 1e-15, "two-key LSE")
+    # causal, two queries: row 0 sees key 0 only, row 1 both keys
+    q2 = np.array([[1.0, 0.0], [1.0, 0.0]])
+    o2, lse2 = orc.attention(q2, k, v, causal=True, scale=1.0)
+    _close(o2, [[1.0, 0.0], [1 / (1 + e), e / (1 + e)]], 1e-15, "two-key causal weights")
+    _close(lse2, [0.0, math.log1p(e)], 1e-15, "two-key causal LSE")
+
+
+def pin_constant_v(orc):
+    rng = _rng(13)
+    for causal in (False, True):
+        q = rng.standard_normal((2, 2, 24, 8)) * 3
+        k = rng.standard_normal((2, 2, 24, 8)) * 3
+        c = rng.standard_normal(8)
+        v = np.broadcast_to(c, (2, 2, 24, 8)).copy()
+        o, _ = orc.attention(q, k, v, causal=causal, scale=0.4)
+        _close(o, np.broadcast_to(c, o.shape), 1e-14, f"constant V causal={causal}")
+
+
+def pin_q_zero(orc):
+    rng = _rng(14)
+    for Nq, Nkv, causal in [(9, 9, True), (5, 12, True), (7, 11, False)]:
+        d = 6
+        q = np.zeros((Nq, d))
+        k = rng.standard_normal((Nkv, d))
+        v = rng.standard_normal((Nkv, d))
+        o, lse = orc.attention(q, k, v, causal=causal, scale=0.3)
+        for i in range(Nq):
+            n = _visible_count(i, Nq, Nkv, causal)
+            _close(o[i], v[:n].mean(axis=0), 1e-14, f"Q=0 mean row {i}")
+            _close(lse[i], math.log(n), 1e-14, f"Q=0 LSE row {i}")
+
+
+def pin_causal_row0(orc):
+    rng = _rng(15)
+    q = rng.standard_normal((16, 8))
+    k = rng.standard_normal((16, 8))
+    v = rng.standard_normal((16, 8))
+    o, lse = orc.attention(q, k, v, causal=True, scale=0.35)
+    assert np.array_equal(o[0], v[0]), "causal row 0 must equal V[0]"
+    _close(lse[0], 0.35 * float(np.dot(q[0], k[0])), 1e-14, "causal row 0 LSE")
+
+
+def pin_dominant_score(orc):
+    rng = _rng(16)
+    Nq, Nkv, d, js = 4, 10, 4, 6
+    q = np.zeros((Nq, d))
+    q[:, 0] = 1.0
+    q[:, 1:] = rng.standard_normal((Nq, d - 1)) * 0.1
+    k = rng.standard_normal((Nkv, d)) * 0.1
+    k[js] = [45.0, 0.0, 0.0, 0.0]
+    v = rng.standard_normal((Nkv, d))
+    o, lse = orc.attention(q, k, v, causal=False, scale=1.0)
+    _close(o, np.broadcast_to(v[js], o.shape), 1e-14, "dominant key selects its V row")
+    _close(lse, np.full(Nq, 45.0), 1e-12, "dominant key LSE")
+    # scores spread far beyond exp's range (key 0 at -400, the dominant key at
+    # +400): a softmax that does not subtract the true row max overflows.
+    k[0] = [-400.0, 0.0, 0.0, 0.0]
+    k[js] = [400.0, 0.0, 0.0, 0.0]
+    o, lse = orc.attention(q, k, v, causal=False, scale=1.0)
+    _close(o, np.broadcast_to(v[js], o.shape), 1e-14, "wide spread: dominant key selects its V row")
+    _close(lse, np.full(Nq, 400.0), 1e-12, "wide spread: LSE equals the dominant score")
+
+
+def pin_single_key(orc):
+    rng = _rng(17)
+    q = rng.standard_normal((3, 5))
+    k = rng.standard_normal((1, 5))
+    v = rng.standard_normal((1, 5))
+    o, lse = orc.attention(q, k, v, causal=False, scale=0.8)
+    assert np.array_equal(o, np.broadcast_to(v[0], o.shape)), "one key: O = V[0]"
+    _close(lse, 0.8 * (q @ k[0]), 1e-14, "one key: LSE = score")
+
+
+def pin_bounds(orc):
+    rng = _rng(18)
+    Nq, Nkv, d = 12, 20, 7
+    q = rng.standard_normal((Nq, d)) * 2
+    k = rng.standard_normal((Nkv, d)) * 2
+    v = rng.standard_normal((Nkv, d))
+    o, lse = orc.attention(q, k, v, causal=True, scale=0.5)
+    s = 0.5 * (q @ k.T)
+    for i in range(Nq):
+        n = _visible_count(i, Nq, Nkv, True)
+        vis = v[:n]
+        assert np.all(o[i] >= vis.min(axis=0) - 1e-14) and np.all(o[i] <= vis.max(axis=0) + 1e-14)
+        smax = s[i, :n].max()
+        assert smax - 1e-14 <= lse[i] <= smax + math.log(n) + 1e-14, f"LSE bounds row {i}"
+
+
+def pin_linearity(orc):
+    rng = _rng(19)
+    q = rng.standard_normal((2, 1, 15, 6))
+    k = rng.standard_normal((2, 1, 18, 6))
+    v = rng.standard_normal((2, 1, 18, 6))
+    o, lse = orc.attention(q, k, v, causal=True, scale=0.6)
+    o8, lse8 = orc.attention(q, k, v * 8.0, causal=True, scale=0.6)
+    assert np.array_equal(o8, o * 8.0), "O(8V) must equal 8 O(V) exactly"
+    assert np.array_equal(lse8, lse), "LSE must not depend on V"
+
+
+def pin_permutation(orc):
+    rng = _rng(20)
+    q = rng.standard_normal((9, 5))
+    k = rng.standard_normal((14, 5))
+    v = rng.standard_normal((14, 5))
+    perm = rng.permutation(14)
+    o, lse = orc.attention(q, k, v, causal=False, scale=0.7)
+    op, lsep = orc.attention(q, k[perm], v[perm], causal=False, scale=0.7)
+    _close(op, o, 1e-14, "joint permutation of K, V")
+    _close(lsep, lse, 1e-14, "joint permutation LSE")
+
+
+def pin_shift_invariance(orc):
+    # Appending a column (c to every query, 1 to every key) adds scale*c to
+    # every score: O is unchanged, LSE moves by scale*c.  With c large the
+    # exponentials overflow unless the row max is subtracted first.
+    rng = _rng(21)
+    Nq, Nkv, d, scale, c = 6, 9, 4, 0.5, 2000.0
+    q = rng.standard_normal((Nq, d))
+    k = rng.standard_normal((Nkv, d))
+    v = rng.standard_normal((Nkv, d))
+    o, lse = orc.attention(q, k, v, causal=True, scale=scale)
+    q2 = np.concatenate([q, np.full((Nq, 1), c)], axis=1)
+    k2 = np.concatenate([k, np.ones((Nkv, 1))], axis=1)
+    v2 = np.concatenate([v, np.zeros((Nkv, 1))], axis=1)  # one head dimension for q, k and v
+    o2, lse2 = orc.attention(q2, k2, v2, causal=True, scale=scale)
+    _close(o2[:, :d], o, 1e-12, "uniform score shift leaves O unchanged")
+    _close(lse2 - scale * c, lse, 1e-10, "uniform score shift moves LSE by the shift")
+
+
+def pin_merge_identity(orc):
+    rng = _rng(22)
+    Nq, Nkv, d = 7, 30, 8
+    q = rng.standard_normal((Nq, d)) * 1.5
+    k = rng.standard_normal((Nkv, d)) * 1.5
+    v = rng.standard_normal((Nkv, d))
+    o, lse = orc.attention(q, k, v, causal=False, scale=0.4)
+    for a in (1, 7, 15, 29):
+        o1, l1 = orc.attention(q, k[:a], v[:a], causal=False, scale=0.4)
+        o2, l2 = orc.attention(q, k[a:], v[a:], causal=False, scale=0.4)
+        lm = np.logaddexp(l1, l2)
+        om = np.exp(l1 - lm)[:, None] * o1 + np.exp(l2 - lm)[:, None] * o2
+        _close(om, o, what=f"merged O, split at {a}")
+        _close(lm, lse, what=f"merged LSE, split at {a}")
+
+
+def pin_rows_match_full(orc):
+    rng = _rng(23)
+    for causal, Nq, Nkv in [(True, 21, 30), (False, 13, 8)]:
+        d = 9
+        q = rng.standard_normal((Nq, d))
+        k = rng.standard_normal((Nkv, d))
+        v = rng.standard_normal((Nkv, d))
+        o, lse = orc.attention(q, k, v, causal=causal, scale=0.3)
+        rows = np.array([0, Nq - 1, Nq // 2, 3])
+        orow, lrow = orc.attention_rows(q, k, v, rows, causal=causal, scale=0.3)
+        assert np.array_equal(orow, o[rows]) and np.array_equal(lrow, lse[rows]), "rows vs full"
+
+
+def pin_head_independence(orc):
+    rng = _rng(24)
+    q = rng.standard_normal((2, 3, 10, 4))
+    k = rng.standard_normal((2, 3, 12, 4))
+    v = rng.standard_normal((2, 3, 12, 4))
+    o, lse = orc.attention(q, k, v, causal=True, scale=0.5)
+    for b in range(2):
+        for h in range(3):
+            oh, lh = orc.attention(q[b, h], k[b, h], v[b, h], causal=True, scale=0.5)
+            assert np.array_equal(oh, o[b, h]) and np.array_equal(lh, lse[b, h]), "head offsets"
+
+
+def pin_widened_inputs(orc):
+    # the 16-bit entry point equals the fp64 entry point on the decoded values
+    rng = _rng(25)
+    for dtype in ("f16", "bf16"):
+        raw = rng.standard_normal((3, 6, 5)).astype(np.float32)
+        if dtype == "f16":
+            bits = raw.astype(np.float16).view(np.uint16)
+            vals = bits.view(np.float16).astype(np.float64)
+        else:
+            import torch
+            t = torch.from_numpy(raw).to(torch.bfloat16)
+            bits = t.view(torch.int16).numpy().view(np.uint16)
+            vals = t.to(torch.float64).numpy()
+        o_b, l_b = orc.attention(bits[0], bits[1], bits[2], causal=True, scale=0.5, dtype=dtype)
+        o_v, l_v = orc.attention(vals[0], vals[1], vals[2], causal=True, scale=0.5)
+        assert np.array_equal(o_b, o_v) and np.array_equal(l_b, l_v), f"{dtype} inputs"
+
+
+PINS = [
+    pin_widen_f16, pin_widen_bf16, pin_decimal_bruteforce, pin_torch_sdpa, pin_two_key_worked,
+    pin_constant_v, pin_q_zero, pin_causal_row0, pin_dominant_score, pin_single_key, pin_bounds,
+    pin_linearity, pin_permutation, pin_shift_invariance, pin_merge_identity, pin_rows_match_full,
+    pin_head_independence, pin_widened_inputs,
+]

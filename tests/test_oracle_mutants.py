@@ -1,0 +1,50 @@
+"""Planted mistakes in the fp64 reference must be caught by its pins.
+
+Each case copies attn_oracle.c, applies one plausible slip (a dropped term, a
+wrong sign or index, an off-by-one mask, a wrong exponent bias), builds the
+copy with gcc into a temporary directory and runs every pin against it.  At
+least one pin has to fail.  The real source is never modified.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+MUTANTS = [
+    ("lse drops the row max", "return m + log(l);", "return log(l);"),
+    ("causal mask excludes the diagonal", "return !causal || j <= i + (Nkv - Nq);",
+     "return !causal || j < i + (Nkv - Nq);"),
+    ("causal mask aligned top-left", "return !causal || j <= i + (Nkv - Nq);",
+     "return !causal || j <= i;"),
+    ("scale not applied", "s_row[j] = scale * dot;", "s_row[j] = dot;"),
+    ("dot product drops its last term", "dot += qi[c] * k[j * d + c];",
+     "dot += (c + 1 < d) ? qi[c] * k[j * d + c] : 0.0;"),
+    ("probabilities not normalised", "s_row[j] = s_row[j] / l;", "s_row[j] = s_row[j];"),
+    ("wrong sign in the exponent", "s_row[j] = exp(s_row[j] - m);", "s_row[j] = exp(m - s_row[j]);"),
+    ("max shift dropped", "s_row[j] = exp(s_row[j] - m);", "s_row[j] = exp(s_row[j]);"),
+    ("value column transposed", "oi[c] += p * v[j * d + c];", "oi[c] += p * v[j * d + (d - 1 - c)];"),
+    ("bf16 exponent bias off by one", "expo - 134", "expo - 133"),
+    ("f16 subnormal scale wrong", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    ("max over visible keys skipped", "if (s_row[j] > m)", "if (j == 0 && s_row[j] > m)"),
+]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("what,find,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, what, find, repl):
+    src = open(oracle.SOURCE).read()
+    assert src.count(find) == 1, f"mutation anchor not found once: {find!r}"
+    mutated = tmp_path / "attn_oracle_mutant.c"
+    mutated.write_text(src.replace(find, repl))
+    lib = oracle.build(str(mutated), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append(f"{pin.__name__}: {type(e).__name__}")
+    assert caught, f"no pin caught the planted mistake: {what}"
