@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of libfa355 on one MI355X.
+
+One step is one pass of the whole hot path on synthetic inputs already
+resident in HBM:
+  1. fa_fwd   on the long-context prefill: B=1, H=32, Nq=Nkv=8192, d=128,
+              fp16, causal, scale 1/sqrt(128), Q and K ~ 1.5 N(0,1), V ~ N(0,1);
+  2. fa_decode on the decode workload: B=16, H=32, one query against
+              Nkv=32768 cached keys, d=128, fp16, split-KV.
+Each call is bracketed by HIP events on the stream it is launched on.  The
+headline value is prefill TFLOP/s (4*B*H*N^2*d FLOPs halved for causal, over
+the mean kernel time); decode is reported in HBM GB/s over its algorithmic
+bytes (K and V once, q, o and lse).  rank 0 prints one JSON line.
+
+The CPU baseline is the fp64 oracle (plain standard attention that
+materialises the score matrix) timed on a sample of the prefill heads on the
+host's cores; it is a reference point, not the target.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd attention TFLOP/s & % MFMA peak, N=8192 d=128 causal; decode HBM GB/s"
+PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
+PREFILL = "prefill_8k_d128"
+DECODE = "decode_32k_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = ["exact_io_aware_65_amd/csrc/fa_fwd.hip", "exact_io_aware_65_amd/csrc/fa_decode.hip",
+                  "exact_io_aware_65_amd/csrc/fa_device.hpp"]
+
+
+# ---------------------------------------------------------------------------
+# FLOP and byte models
+
+def metric_flops(B, H, Nq, Nkv, d, causal):
+    """The method's contraction FLOPs, 2 * (QK^T + PV); halved for a causal mask."""
+    f = 4 * B * H * Nq * Nkv * d
+    return f // 2 if causal else f
+
+
+def algorithmic_bytes(B, H, Nq, Nkv, d, elt=2, out_elt=2, lse=True):
+    """Compulsory HBM traffic: read q, k, v once; write o (and lse) once."""
+    return elt * B * H * (Nq + 2 * Nkv) * d + out_elt * B * H * Nq * d + (4 * B * H * Nq if lse else 0)
+
+
+def score_matrix_bytes(n, elt=2):
+    """Bytes of one head's n x n score matrix: what the fused kernel never writes."""
+    return n * n * elt
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.loads(f.read().split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec
+
+
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, x, target_s=12.0):
+    """The oracle on a sample of the prefill heads: time one head, then enough to fill ~target_s."""
+    import oracle
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < w.heads:
+        b, h = divmod(heads, w.H)
+        oracle.attention(x["q"][b, h], x["k"][b, h], x["v"][b, h], causal=w.causal, scale=w.scale,
+                         dtype=w.dtype)
+        heads += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = metric_flops(1, heads, w.Nq, w.Nkv, w.d, w.causal)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.heads} heads of {w.name} (fp64, score matrix materialised), {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = library choice)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+                  "(the kernels shard by head with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import exact_io_aware_65_amd as fa
+    import fa_inputs as fi
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    pw, dw = fi.WORKLOADS[PREFILL], fi.WORKLOADS[DECODE]
+
+    log(f"generating {PREFILL}")
+    px = fi.make_inputs(pw)
+    pq, pk, pv = (fi.bits_to_torch(px[t], pw.dtype).to(dev) for t in "qkv")
+    log(f"generating {DECODE}")
+    dx = fi.make_inputs(dw)
+    dq, dk, dv = (fi.bits_to_torch(dx[t], dw.dtype).to(dev) for t in "qkv")
+    dx = None  # decode inputs are not needed on the host any more
+
+    po = torch.empty_like(pq)
+    plse = torch.empty((pw.B, pw.H, pw.Nq), dtype=torch.float32, device=dev)
+    do = torch.empty_like(dq)
+    dlse = torch.empty((dw.B, dw.H), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_decode_workspace_size(dw.B, dw.H, dw.Nkv, dw.d, args.num_splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    splits = fa.fa_decode_num_splits(dw.B, dw.H, dw.Nkv, dw.d) if args.num_splits == 0 else \
+        ws_bytes // (dw.B * dw.H * (dw.d + 1) * 4)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def step(ev):
+        ev[0].record(stream)
+        fa.fa_fwd(pq, pk, pv, po, plse, pw.B, pw.H, pw.Nq, pw.Nkv, pw.d, pw.causal, pw.scale, fa.FA_F16, sp)
+        ev[1].record(stream)
+        fa.fa_decode(dq, dk, dv, do, dlse, dw.B, dw.H, dw.Nkv, dw.d, dw.scale, fa.FA_F16, args.num_splits,
+                     ws, ws_bytes, sp)
+        ev[2].record(stream)
+
+    def events():
+        return tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(events())
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    dec_ms = [b.elapsed_time(c) for _, b, c in evs]
+
+    p_flops = metric_flops(pw.B, pw.H, pw.Nq, pw.Nkv, pw.d, pw.causal)
+    p_bytes = algorithmic_bytes(pw.B, pw.H, pw.Nq, pw.Nkv, pw.d)
+    d_bytes = algorithmic_bytes(dw.B, dw.H, 1, dw.Nkv, dw.d)
+    fwd_mean = statistics.fmean(fwd_ms)
+    dec_mean = statistics.fmean(dec_ms)
+    tflops = p_flops / (fwd_mean * 1e-3) / 1e12
+    gbs = d_bytes / (dec_mean * 1e-3) / 1e9
+
+    def pct(xs, q):
+        xs = sorted(xs)
+        return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{PREFILL} + {DECODE}",
+            "prefill": {"B": pw.B, "H": pw.H, "Nq": pw.Nq, "Nkv": pw.Nkv, "d": pw.d, "causal": pw.causal,
+                        "dtype": pw.dtype, "seed": pw.seed, "sigma_qk": pw.sigma_qk},
+            "decode": {"B": dw.B, "H": dw.H, "Nq": 1, "Nkv": dw.Nkv, "d": dw.d, "dtype": dw.dtype,
+                       "seed": dw.seed, "num_splits": splits},
+        },
+        "roofline": {
+            "kernel": "fwd_kernel<128, f16, causal>",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_MFMA_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
+            "traffic": traffic["prefill_bytes"] if traffic else None,
+        },
+        "roofline_decode": {
+            "kernel": "decode_split_kernel<128, f16> + decode_combine_kernel",
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic["decode_bytes"] if traffic else None,
+        },
+        "prefill": {"ms_mean": round(fwd_mean, 4), "ms_p10": round(pct(fwd_ms, 0.1), 4),
+                    "ms_p50": round(pct(fwd_ms, 0.5), 4), "ms_p90": round(pct(fwd_ms, 0.9), 4),
+                    "flops": p_flops, "algorithmic_bytes": p_bytes},
+        "decode": {"ms_mean": round(dec_mean, 4), "ms_p10": round(pct(dec_ms, 0.1), 4),
+                   "ms_p50": round(pct(dec_ms, 0.5), 4), "ms_p90": round(pct(dec_ms, 0.9), 4),
+                   "GB/s": round(gbs, 1), "algorithmic_bytes": d_bytes, "workspace_bytes": ws_bytes},
+        "gpu": {"name": props.name, "cus": props.multi_processor_count,
+                "arch": getattr(props, "gcnArchName", "")},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(pw, px)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

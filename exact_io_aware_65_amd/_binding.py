@@ -1,0 +1,184 @@
+"""ctypes binding of libfa355 (include/fa355.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libfa355.so.  PyTorch supplies device memory and the current
+stream.  The library must have been built (``python -m
+exact_io_aware_65_amd.build``); there is no fallback of any kind.
+
+Thin wrappers with the C names (``fa_fwd``, ``fa_decode``, ...) take device
+pointers or tensors and raise :class:`FaError` on a non-OK status.  The
+convenience functions :func:`fwd` and :func:`decode` allocate the outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
+
+FA_F16 = 1
+FA_BF16 = 2
+FA_OUT_F32 = 0x100
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{fa_status_str(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libfa355.so (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError(f"{LIBRARY} is missing: build it with `python -m exact_io_aware_65_amd.build`")
+        lib = ctypes.CDLL(LIBRARY)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        lib.fa_decode.restype = i
+        lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
+        lib.fa_decode_workspace_size.restype = ctypes.c_size_t
+        lib.fa_decode_num_splits.argtypes = [i, i, i, i]
+        lib.fa_decode_num_splits.restype = i
+        lib.fa_status_str.argtypes = [i]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        lib.fa_last_error.restype = ctypes.c_char_p
+        lib.fa_version.restype = i
+        _lib = lib
+    return _lib
+
+
+def _addr(x):
+    """Device address of a tensor (or an int / None passed through)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status, fa_last_error())
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, one to one
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, dtype, stream=None) -> None:
+    _check(library().fa_fwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, H, Nq, Nkv, d,
+                            int(bool(causal)), float(scale), int(dtype), _addr(stream)))
+
+
+def fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, dtype, num_splits, workspace, workspace_bytes,
+              stream=None) -> None:
+    _check(library().fa_decode(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, H, Nkv, d,
+                               float(scale), int(dtype), int(num_splits), _addr(workspace),
+                               int(workspace_bytes), _addr(stream)))
+
+
+def fa_decode_workspace_size(B, H, Nkv, d, num_splits=0) -> int:
+    return int(library().fa_decode_workspace_size(B, H, Nkv, d, num_splits))
+
+
+def fa_decode_num_splits(B, H, Nkv, d) -> int:
+    return int(library().fa_decode_num_splits(B, H, Nkv, d))
+
+
+def fa_status_str(status: int) -> str:
+    return library().fa_status_str(status).decode()
+
+
+def fa_last_error() -> str:
+    return library().fa_last_error().decode()
+
+
+def fa_version() -> int:
+    return int(library().fa_version())
+
+
+# ---------------------------------------------------------------------------
+# tensor conveniences
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"q, k, v must be float16 or bfloat16, got {t.dtype}")
+
+
+def _stream(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def fwd(q, k, v, *, causal=False, scale=None, out_dtype=None, with_lse=True):
+    """O = softmax(scale * q k^T [causal]) v and LSE for [B, H, N, d] tensors.
+
+    Returns (o, lse); lse is None when with_lse is False.  out_dtype may be
+    torch.float32 to get O in fp32, else O has q's dtype."""
+    import torch
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    code = _dtype_code(q)
+    odt = q.dtype
+    if out_dtype is not None and out_dtype != q.dtype:
+        if out_dtype != torch.float32:
+            raise TypeError("out_dtype must be None, q.dtype or torch.float32")
+        code |= FA_OUT_F32
+        odt = torch.float32
+    o = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if with_lse else None
+    fa_fwd(q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, code, _stream(q.device))
+    return o, lse
+
+
+def decode(q, k, v, *, scale=None, num_splits=0, out_dtype=None):
+    """One query per (b, h): q [B, H, d] (or [B, H, 1, d]), k/v [B, H, Nkv, d].
+
+    Returns (o, lse) with o shaped like q."""
+    import torch
+    _check_inputs(q, k, v)
+    B, H, Nkv, d = k.shape
+    if v.shape != k.shape or q.numel() != B * H * d or q.shape[:2] != (B, H):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    code = _dtype_code(q)
+    odt = q.dtype
+    if out_dtype is not None and out_dtype != q.dtype:
+        if out_dtype != torch.float32:
+            raise TypeError("out_dtype must be None, q.dtype or torch.float32")
+        code |= FA_OUT_F32
+        odt = torch.float32
+    o = torch.empty(q.shape, dtype=odt, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nbytes = fa_decode_workspace_size(B, H, Nkv, d, num_splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, code, num_splits, ws, nbytes, _stream(q.device))
+    return o, lse

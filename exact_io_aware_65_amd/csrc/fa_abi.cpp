@@ -1,0 +1,230 @@
+// C ABI of libfa355 (declared in include/fa355.h): argument validation,
+// split-count resolution and dispatch to the kernel launchers.  Every check
+// runs on the host before any HIP call, so a rejected call touches neither
+// the device nor the outputs.
+#include "fa355.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "fa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("FA355_LOG");
+        return e && *e && *e != '0';
+    }();
+    return on;
+}
+
+struct Span {
+    const char *name;
+    std::uintptr_t lo, hi;
+};
+
+bool overlap(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Span span(const char *name, const void *p, unsigned __int128 bytes)
+{
+    const auto lo = reinterpret_cast<std::uintptr_t>(p);
+    return {name, lo, lo + static_cast<std::uintptr_t>(bytes)};
+}
+
+bool misaligned(const void *p, std::uintptr_t align)
+{
+    return reinterpret_cast<std::uintptr_t>(p) % align != 0;
+}
+
+// dtype = element type, optionally OR-ed with FA_OUT_F32.
+int parse_dtype(const char *fn, int dtype, fa355::Elem *elem, bool *out_f32)
+{
+    const int base = dtype & 0xff, flags = dtype & ~0xff;
+    if ((base != FA_F16 && base != FA_BF16) || (flags != 0 && flags != FA_OUT_F32))
+        return fail(FA_ERR_INVALID, "%s: dtype 0x%x is not FA_F16 or FA_BF16 (optionally | FA_OUT_F32)",
+                    fn, dtype);
+    *elem = base == FA_F16 ? fa355::Elem::F16 : fa355::Elem::BF16;
+    *out_f32 = flags == FA_OUT_F32;
+    return FA_OK;
+}
+
+int check_head_dim(const char *fn, int d)
+{
+    if (d <= 0) return fail(FA_ERR_INVALID, "%s: head dimension d=%d must be positive", fn, d);
+    if (d != 64 && d != 128)
+        return fail(FA_ERR_UNSUPPORTED, "%s: head dimension d=%d is not supported (64 or 128)", fn, d);
+    return FA_OK;
+}
+
+constexpr unsigned __int128 kMaxElems = static_cast<unsigned __int128>(1) << 62;
+
+// Checks shared by fa_fwd and fa_decode once there is work to do.
+int check_tensors(const char *fn, const void *q, const void *k, const void *v, const void *o,
+                  const float *lse, int B, int H, int Nq, int Nkv, int d, bool out_f32)
+{
+    if (!q || !k || !v || !o) return fail(FA_ERR_INVALID, "%s: q, k, v and o must be non-NULL", fn);
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
+        return fail(FA_ERR_INVALID, "%s: q, k, v and o must be 16-byte aligned", fn);
+    if (lse && misaligned(lse, 4)) return fail(FA_ERR_INVALID, "%s: lse must be 4-byte aligned", fn);
+    const unsigned __int128 bh = static_cast<unsigned __int128>(B) * H;
+    const unsigned __int128 nq_el = bh * Nq * d, nkv_el = bh * Nkv * d;
+    if (nq_el >= kMaxElems || nkv_el >= kMaxElems)
+        return fail(FA_ERR_INVALID, "%s: tensor sizes exceed 2^62 elements", fn);
+    const Span in[3] = {span("q", q, nq_el * 2), span("k", k, nkv_el * 2), span("v", v, nkv_el * 2)};
+    const Span out_o = span("o", o, nq_el * (out_f32 ? 4 : 2));
+    for (const Span &s : in)
+        if (overlap(out_o, s)) return fail(FA_ERR_INVALID, "%s: o overlaps %s", fn, s.name);
+    if (lse) {
+        const Span out_l = span("lse", lse, bh * Nq * 4);
+        for (const Span &s : in)
+            if (overlap(out_l, s)) return fail(FA_ERR_INVALID, "%s: lse overlaps %s", fn, s.name);
+        if (overlap(out_l, out_o)) return fail(FA_ERR_INVALID, "%s: lse overlaps o", fn);
+    }
+    return FA_OK;
+}
+
+// Split count actually used for (Nkv, requested); each split holds >= 1 key.
+void resolve_splits(int B, int H, int Nkv, int d, int requested, int *splits, int *chunk)
+{
+    int s = requested > 0 ? requested : fa355::decode_auto_splits(B, H, Nkv, d);
+    if (s > Nkv) s = Nkv;
+    const int c = (Nkv + s - 1) / s;
+    *chunk = c;
+    *splits = (Nkv + c - 1) / c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nq,
+           int Nkv, int d, int causal, float scale, int dtype, hipStream_t stream)
+{
+    static const char *fn = "fa_fwd";
+    fa355::Elem elem;
+    bool out_f32;
+    int rc = parse_dtype(fn, dtype, &elem, &out_f32);
+    if (rc) return rc;
+    if ((rc = check_head_dim(fn, d))) return rc;
+    if (B < 0 || H < 0 || Nq < 0 || Nkv < 0)
+        return fail(FA_ERR_INVALID, "%s: negative size (B=%d H=%d Nq=%d Nkv=%d)", fn, B, H, Nq, Nkv);
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "%s: scale must be finite", fn);
+    if (B == 0 || H == 0 || Nq == 0) return FA_OK;  // empty output: nothing to do
+    if (Nkv == 0) return fail(FA_ERR_INVALID, "%s: Nkv=0: attention over no keys is undefined", fn);
+    if (causal && Nq > Nkv)
+        return fail(FA_ERR_INVALID, "%s: causal attention needs Nq <= Nkv (got %d > %d)", fn, Nq, Nkv);
+    if ((rc = check_tensors(fn, q, k, v, o, lse, B, H, Nq, Nkv, d, out_f32))) return rc;
+    const int rows = fa355::fwd_rows_per_block(d);
+    const long long blocks = static_cast<long long>(B) * H * ((Nq + rows - 1) / rows);
+    if (blocks > 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+
+    fa355::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nkv, d, causal != 0, scale, elem, out_f32};
+    if (log_enabled())
+        std::fprintf(stderr, "fa355: fa_fwd B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x grid=%lld\n",
+                     B, H, Nq, Nkv, d, causal != 0, dtype, blocks);
+    const hipError_t err = fa355::launch_fwd(a, stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return FA_OK;
+}
+
+size_t fa_decode_workspace_size(int B, int H, int Nkv, int d, int num_splits)
+{
+    if (B < 0 || H < 0 || Nkv < 1 || (d != 64 && d != 128) || num_splits < 0) return 0;
+    if (B == 0 || H == 0) return 0;
+    int splits, chunk;
+    resolve_splits(B, H, Nkv, d, num_splits, &splits, &chunk);
+    return fa355::decode_workspace_bytes(B, H, splits, d);
+}
+
+int fa_decode_num_splits(int B, int H, int Nkv, int d)
+{
+    if (B < 0 || H < 0 || Nkv < 1 || (d != 64 && d != 128)) return 0;
+    int splits, chunk;
+    resolve_splits(B, H, Nkv, d, 0, &splits, &chunk);
+    return splits;
+}
+
+int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nkv,
+              int d, float scale, int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+              hipStream_t stream)
+{
+    static const char *fn = "fa_decode";
+    fa355::Elem elem;
+    bool out_f32;
+    int rc = parse_dtype(fn, dtype, &elem, &out_f32);
+    if (rc) return rc;
+    if ((rc = check_head_dim(fn, d))) return rc;
+    if (B < 0 || H < 0 || Nkv < 0)
+        return fail(FA_ERR_INVALID, "%s: negative size (B=%d H=%d Nkv=%d)", fn, B, H, Nkv);
+    if (num_splits < 0) return fail(FA_ERR_INVALID, "%s: num_splits=%d must be >= 0", fn, num_splits);
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "%s: scale must be finite", fn);
+    if (B == 0 || H == 0) return FA_OK;
+    if (Nkv == 0) return fail(FA_ERR_INVALID, "%s: Nkv=0: attention over no keys is undefined", fn);
+    if ((rc = check_tensors(fn, q, k, v, o, lse, B, H, 1, Nkv, d, out_f32))) return rc;
+
+    int splits, chunk;
+    resolve_splits(B, H, Nkv, d, num_splits, &splits, &chunk);
+    const long long blocks = static_cast<long long>(B) * H * splits;
+    if (blocks > 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+    const size_t need = fa355::decode_workspace_bytes(B, H, splits, d);
+    if (!workspace || misaligned(workspace, 16) || workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)",
+                    fn, need, workspace_bytes, workspace);
+    const unsigned __int128 n_in = static_cast<unsigned __int128>(B) * H * d;
+    const unsigned __int128 n_kv = static_cast<unsigned __int128>(B) * H * Nkv * d;
+    const Span ws = span("workspace", workspace, need);
+    const Span others[5] = {span("q", q, n_in * 2), span("k", k, n_kv * 2), span("v", v, n_kv * 2),
+                            span("o", o, n_in * (out_f32 ? 4 : 2)),
+                            span("lse", lse, lse ? static_cast<unsigned __int128>(B) * H * 4 : 0)};
+    for (const Span &s : others)
+        if (s.hi > s.lo && overlap(ws, s)) return fail(FA_ERR_WORKSPACE, "%s: workspace overlaps %s", fn, s.name);
+
+    float *ws_o = static_cast<float *>(workspace);
+    float *ws_lse = ws_o + static_cast<size_t>(B) * H * splits * d;
+    fa355::DecodeArgs a{q, k, v, o, lse, B, H, Nkv, d, scale, elem, out_f32, splits, chunk, ws_o, ws_lse};
+    if (log_enabled())
+        std::fprintf(stderr, "fa355: fa_decode B=%d H=%d Nkv=%d d=%d dtype=0x%x splits=%d chunk=%d\n", B, H,
+                     Nkv, d, dtype, splits, chunk);
+    const hipError_t err = fa355::launch_decode(a, stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return FA_OK;
+}
+
+const char *fa_status_str(int status)
+{
+    switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_ERR_UNKNOWN";
+    }
+}
+
+const char *fa_last_error(void) { return g_last_error.c_str(); }
+
+int fa_version(void) { return FA355_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,220 @@
+// Split-KV decode for gfx950: one query per (batch, head) against a long
+// key/value cache ("Flash Attention -- Module 12.3", section "Prefill vs
+// Decode").  A single query row leaves the matrix cores nothing to tile, so
+// the path is a stream: its speed is the rate at which K and V leave HBM.
+//
+// Pass 1 (split kernel): the cache of every head is cut into `splits` chunks
+// processed by independent workgroups ("FlashAttention 1-2-3: The IO-Aware
+// Revolution in LLM Inference", section "Beyond FlashAttention: Future
+// Directions and Alternatives": parallelise over the cache length, then
+// reduce).  Inside a workgroup, each group of d/8 lanes owns a stream of
+// keys; a lane holds 8 dimensions of q and reads the matching 16 bytes of
+// every K and V row, so each wave-wide load covers whole consecutive rows.
+// Scores come from packed 16-bit dot products with fp32 accumulation and a
+// DPP reduction across the group; the group keeps its own online-softmax
+// state (m, l, 8 accumulators per lane).  The groups are merged through LDS
+// and the chunk's normalised partial output and base-2 log-sum-exp go to the
+// workspace.
+//
+// Pass 2 (combine kernel): per head, the partial results are merged exactly
+// by their log-sum-exp values, the two-block merge of "FlashAttention 1-2-3
+// ...", section "The Math Behind the Online Softmax Trick", applied to all
+// chunks at once: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa355 {
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecUnroll = 8;  // key rows in flight per lane group per iteration
+
+struct SplitParams {
+    const void *q, *k, *v;
+    float *ws_o, *ws_lse;
+    int Nkv, chunk, splits;
+    float scale_log2;
+};
+
+template <int D, typename T>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParams p)
+{
+    constexpr int LPK = D / 8;                 // lanes per key row
+    constexpr int KPI = 64 / LPK;              // key rows per wave-wide load
+    constexpr int GROUPS = kDecWaves * KPI;    // independent key streams per workgroup
+    constexpr int STEP = GROUPS * kDecUnroll;  // keys per workgroup iteration
+
+    const int split = blockIdx.x % p.splits;
+    const int bh = blockIdx.x / p.splits;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane / LPK, r = lane % LPK;
+    const int grp = w * KPI + g;
+    const int ks = split * p.chunk;
+    const int ke = min(p.Nkv, ks + p.chunk);
+
+    const size_t kvbase = static_cast<size_t>(bh) * p.Nkv * D + 8 * r;
+    const T *Kg = static_cast<const T *>(p.k) + kvbase;
+    const T *Vg = static_cast<const T *>(p.v) + kvbase;
+    const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(p.q) + static_cast<size_t>(bh) * D + 8 * r);
+
+    float m = -INFINITY, l = 0.f;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+
+    for (int base = ks; base < ke; base += STEP) {
+        u32x4 kr[kDecUnroll], vr[kDecUnroll];
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const int key = base + u * GROUPS + grp;
+            u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+            if (key < ke) {
+                kx = *reinterpret_cast<const u32x4 *>(Kg + static_cast<size_t>(key) * D);
+                vx = *reinterpret_cast<const u32x4 *>(Vg + static_cast<size_t>(key) * D);
+            }
+            kr[u] = kx;
+            vr[u] = vx;
+        }
+        float t[kDecUnroll];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s = dot2<T>(qv[j], kr[u][j], s);
+            s = group_sum<LPK>(s);
+            const int key = base + u * GROUPS + grp;
+            t[u] = key < ke ? s * p.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, t[u]);
+        }
+        const float m_new = fmaxf(m, mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m - m_ref);
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+            const float pu = fast_exp2(t[u] - m_ref);
+            l += pu;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] += pu * lo_f32<T>(vr[u][j]);
+                acc[2 * j + 1] += pu * hi_f32<T>(vr[u][j]);
+            }
+        }
+        m = m_new;
+    }
+
+    // merge the workgroup's key streams
+    __shared__ float s_m[GROUPS], s_l[GROUPS];
+    __shared__ float s_acc[GROUPS][D];
+    if (r == 0) {
+        s_m[grp] = m;
+        s_l[grp] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_acc[grp][8 * r + j] = acc[j];
+    __syncthreads();
+    if (tid < D) {
+        float M = -INFINITY;
+        for (int G = 0; G < GROUPS; ++G) M = fmaxf(M, s_m[G]);
+        float L = 0.f, o = 0.f;
+        for (int G = 0; G < GROUPS; ++G) {
+            const float wgt = fast_exp2(s_m[G] - M);  // 0 for a stream that saw no key
+            L += s_l[G] * wgt;
+            o += s_acc[G][tid] * wgt;
+        }
+        const size_t slot = static_cast<size_t>(bh) * p.splits + split;
+        p.ws_o[slot * D + tid] = o / L;
+        if (tid == 0) p.ws_lse[slot] = M + __builtin_amdgcn_logf(L);
+    }
+}
+
+struct CombineParams {
+    const float *ws_o, *ws_lse;
+    void *o;
+    float *lse;
+    int splits;
+};
+
+template <int D, typename TO>
+__global__ __launch_bounds__(D) void decode_combine_kernel(CombineParams p)
+{
+    const int bh = blockIdx.x, d = threadIdx.x;
+    const float *L = p.ws_lse + static_cast<size_t>(bh) * p.splits;
+    const float *O = p.ws_o + static_cast<size_t>(bh) * p.splits * D + d;
+    float M = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, L[s]);
+    float den = 0.f, num = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+        const float wgt = fast_exp2(L[s] - M);
+        den += wgt;
+        num += wgt * O[static_cast<size_t>(s) * D];
+    }
+    static_cast<TO *>(p.o)[static_cast<size_t>(bh) * D + d] = static_cast<TO>(num / den);
+    if (d == 0 && p.lse) p.lse[bh] = (M + __builtin_amdgcn_logf(den)) * kLn2;
+}
+
+template <int D, typename T>
+hipError_t launch(const DecodeArgs &a, hipStream_t stream)
+{
+    const int n_bh = a.B * a.H;
+    SplitParams sp;
+    sp.q = a.q;
+    sp.k = a.k;
+    sp.v = a.v;
+    sp.ws_o = a.ws_o;
+    sp.ws_lse = a.ws_lse;
+    sp.Nkv = a.Nkv;
+    sp.chunk = a.chunk;
+    sp.splits = a.splits;
+    sp.scale_log2 = a.scale * kLog2e;
+    const dim3 grid1(static_cast<unsigned>(static_cast<long long>(n_bh) * a.splits));
+    hipLaunchKernelGGL((decode_split_kernel<D, T>), grid1, dim3(64 * kDecWaves), 0, stream, sp);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    CombineParams cp;
+    cp.ws_o = a.ws_o;
+    cp.ws_lse = a.ws_lse;
+    cp.o = a.o;
+    cp.lse = a.lse;
+    cp.splits = a.splits;
+    if (a.out_f32)
+        hipLaunchKernelGGL((decode_combine_kernel<D, float>), dim3(n_bh), dim3(D), 0, stream, cp);
+    else
+        hipLaunchKernelGGL((decode_combine_kernel<D, T>), dim3(n_bh), dim3(D), 0, stream, cp);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
+{
+    return a.elem == Elem::F16 ? launch<D, _Float16>(a, stream) : launch<D, __bf16>(a, stream);
+}
+
+}  // namespace
+
+int decode_auto_splits(int B, int H, int Nkv, int /*d*/)
+{
+    // About 2K keys per split, and enough workgroups to give every CU several.
+    const long long n_bh = static_cast<long long>(B) * H;
+    long long s = (Nkv + 2047) / 2048;
+    const long long want_blocks = 2048;
+    if (n_bh * s < want_blocks) s = (want_blocks + n_bh - 1) / n_bh;
+    const long long max_s = (Nkv + 127) / 128;  // keep at least ~128 keys per split
+    if (s > max_s) s = max_s;
+    if (s > 256) s = 256;
+    if (s < 1) s = 1;
+    return static_cast<int>(s);
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
+{
+    if (a.d == 64) return launch_d<64>(a, stream);
+    if (a.d == 128) return launch_d<128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa355

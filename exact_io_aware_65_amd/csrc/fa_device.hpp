@@ -1,0 +1,142 @@
+// Device-side building blocks for gfx950 (CDNA4, wave64): vector types, the
+// 32x32x16 MFMA, 16-bit conversions and cross-lane exchanges.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fa355 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage element traits: 8-wide operand vector and conversions.
+template <typename T> struct Vec;
+template <> struct Vec<_Float16> {
+    using v8 = f16x8;
+    using v2 = f16x2;
+};
+template <> struct Vec<__bf16> {
+    using v8 = bf16x8;
+    using v2 = bf16x2;
+};
+
+// D(32x32, fp32) += A(32x16) * B(16x32).  Lane l supplies row (A) or column (B)
+// l % 32 and eight consecutive k-slots chosen by l / 32; it receives column
+// l % 32 of D, rows 8*(e/4) + 4*(l/32) + e%4 for accumulator element e.
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename V> __device__ __forceinline__ V as(u32x4 x) { return __builtin_bit_cast(V, x); }
+
+// Round-to-nearest-even conversions of fp32 pairs to the storage type,
+// returned as one packed 32-bit word (low half = first value).
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b)
+{
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b)
+{
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Widen the low / high 16-bit element of a packed word to fp32 (exact).
+template <typename T> __device__ __forceinline__ float lo_f32(uint32_t w);
+template <typename T> __device__ __forceinline__ float hi_f32(uint32_t w);
+template <> __device__ __forceinline__ float lo_f32<_Float16>(uint32_t w)
+{
+    return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+template <> __device__ __forceinline__ float hi_f32<_Float16>(uint32_t w)
+{
+    return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+template <> __device__ __forceinline__ float lo_f32<__bf16>(uint32_t w)
+{
+    return __builtin_bit_cast(float, w << 16);
+}
+template <> __device__ __forceinline__ float hi_f32<__bf16>(uint32_t w)
+{
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi with fp32 accumulation (v_dot2c_f32_{f16,bf16}).
+template <typename T> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc);
+template <> __device__ __forceinline__ float dot2<_Float16>(uint32_t a, uint32_t b, float acc)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                  false);
+}
+template <> __device__ __forceinline__ float dot2<__bf16>(uint32_t a, uint32_t b, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// The pair (1, 1) in the storage type, for row sums via dot2.
+template <typename T> inline constexpr uint32_t kOnePair = 0;
+template <> inline constexpr uint32_t kOnePair<_Float16> = 0x3C003C00u;
+template <> inline constexpr uint32_t kOnePair<__bf16> = 0x3F803F80u;
+
+// 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// {x of this lane, x of lane ^ 32} in some order (v_permlane32_swap).  Any
+// symmetric combination (max, sum) of the pair is the same in both lanes.
+__device__ __forceinline__ float max_with_other_half(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                              __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ __forceinline__ float sum_with_other_half(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                              __builtin_bit_cast(uint32_t, x), false, false);
+    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+
+// DPP lane exchanges inside a 16-lane row.
+enum : int {
+    kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+    kDppHalfMirror = 0x141, // lane i <-> 7 - i within each half row
+    kDppMirror = 0x140      // lane i <-> 15 - i within the row
+};
+template <int CTRL> __device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane of the group gets the sum.
+template <int N> __device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(N == 8 || N == 16, "group size");
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    if constexpr (N == 16) x += dpp<kDppMirror>(x);
+    return x;
+}
+
+}  // namespace fa355

@@ -1,0 +1,55 @@
+// Internal interface between the C ABI layer (fa_abi.cpp) and the kernel
+// launchers (fa_fwd.hip, fa_decode.hip).  Arguments arrive here already
+// validated; launchers only pick a template instance, size the grid and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace fa355 {
+
+enum class Elem { F16 = 1, BF16 = 2 };
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;  // may be null
+    int B, H, Nq, Nkv, d;
+    bool causal;
+    float scale;
+    Elem elem;
+    bool out_f32;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;  // may be null
+    int B, H, Nkv, d;
+    float scale;
+    Elem elem;
+    bool out_f32;
+    int splits;      // resolved split count, each split non-empty
+    int chunk;       // keys per split (the last split may hold fewer)
+    float *ws_o;     // [B*H][splits][d] normalised partial outputs
+    float *ws_lse;   // [B*H][splits] partial log2-sum-exp values
+};
+
+// Query rows handled by one prefill workgroup (depends on d).
+int fwd_rows_per_block(int d);
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+// Split count used when the caller passes num_splits = 0.
+int decode_auto_splits(int B, int H, int Nkv, int d);
+
+// Workspace bytes for a resolved split count.
+inline std::size_t decode_workspace_bytes(int B, int H, int splits, int d)
+{
+    return static_cast<std::size_t>(B) * H * splits * (d + 1) * sizeof(float);
+}
+
+}  // namespace fa355

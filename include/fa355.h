@@ -1,0 +1,153 @@
+/*
+ * fa355.h -- C ABI of libfa355: exact, IO-aware fused softmax attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every batch b, head h and query row i:
+ *
+ *     O[i]   = sum_j softmax_j(scale * q[i] . k[j]) * v[j]
+ *     LSE[i] = ln sum_j exp(scale * q[i] . k[j])
+ *
+ * with j ranging over the keys visible to row i.  This is standard attention
+ * S = Q K^T, P = softmax(S), O = P V ("FlashAttention", section "The problem:
+ * the n x n score matrix"; the 1/sqrt(d) of "Flash Attention -- Module 12.3",
+ * section "Definition", is the caller's `scale`).  The library computes it the
+ * IO-aware way: Q, K and V are streamed tile by tile through on-chip memory and
+ * the softmax is taken online, keeping a running row maximum m and running
+ * denominator l and rescaling the partial output whenever m grows
+ * ("FlashAttention", sections "The fix: tile through SRAM, fuse the passes" and
+ * "Online softmax: the enabling trick"), so the Nq x Nkv score matrix never
+ * reaches device memory.  The result equals the definition up to floating-point
+ * rounding ("Flash Attention -- Module 12.3", section "Common Misconception").
+ *
+ * LSE is not named on the pages: it is the (m, l) pair the online softmax keeps
+ * per row, folded into one natural-log value m + ln l.  It is what partial
+ * results over disjoint key sets need to be merged exactly ("FlashAttention
+ * 1-2-3: The IO-Aware Revolution in LLM Inference", section "The Math Behind
+ * the Online Softmax Trick").
+ *
+ * Causal masking.  Key j is visible to query row i iff j <= i + (Nkv - Nq):
+ * the lower triangle including the diagonal when Nq == Nkv, aligned to the
+ * last key when Nq < Nkv (a reading; the pages show only square masks).
+ * Blocks of keys that no row of a query tile can see are skipped entirely
+ * ("FlashAttention 1-2-3 ...", section "FlashAttention-2: Reducing Non-Matmul
+ * Overhead and Causal Efficiency").
+ *
+ * Data layout (all arrays row-major and contiguous, head dimension fastest):
+ *     q    [B][H][Nq][d]    k, v [B][H][Nkv][d]    element type `dtype`
+ *     o    [B][H][Nq][d]    element type `dtype`, or float32 with FA_OUT_F32
+ *     lse  [B][H][Nq]       float32 (may be NULL: not written)
+ * fa_decode is the Nq == 1 case: q and o are [B][H][d], lse is [B][H].
+ *
+ * Ownership.  Every pointer is device memory owned by the caller (for example
+ * the storage of framework tensors).  The library allocates no device memory:
+ * fa_fwd needs none, fa_decode uses only the caller's workspace.  No pointer
+ * is retained after a call returns.
+ *
+ * Execution.  Calls enqueue work on `stream` (NULL = the default stream) and
+ * return without waiting; results are ready when the stream is synchronised.
+ * Calls are reentrant and thread-safe.  Results are deterministic: the same
+ * inputs, shapes and split count give bitwise-identical outputs (no atomics).
+ *
+ * Errors.  Every argument is validated on the host before any HIP call; a
+ * violation returns a status code and leaves the outputs untouched.  No
+ * exception or abort crosses the ABI, and there is no silent fallback to a
+ * slower path: an unsupported configuration returns FA_ERR_UNSUPPORTED.  A
+ * failed kernel launch returns FA_ERR_HIP.  fa_last_error() gives the
+ * calling thread's message for its last non-OK return.  Faults inside a
+ * kernel surface, as usual in HIP, at the next synchronisation.
+ *
+ * Preconditions shared by the entry points:
+ *   - q, k, v, o non-NULL and 16-byte aligned; lse, when given, 4-byte aligned;
+ *   - o and lse do not overlap q, k, v or each other;
+ *   - d is 64 or 128 (other head dimensions: FA_ERR_UNSUPPORTED);
+ *   - dtype is FA_F16 or FA_BF16, optionally OR-ed with FA_OUT_F32;
+ *   - scale is finite; inputs are finite (Inf/NaN inputs: undefined results);
+ *   - B, H, Nq >= 0 (a zero makes the call a no-op returning FA_OK);
+ *     Nkv >= 1 whenever there is work (attention over no keys is undefined);
+ *   - causal requires Nq <= Nkv, so every row sees at least one key;
+ *   - B*H*N*d fits in 2^62 elements.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's opaque stream handle (identical to the typedef in hip_runtime_api.h). */
+typedef struct ihipStream_t *hipStream_t;
+
+#define FA355_VERSION 1
+
+/* Element type of q, k, v (and of o unless FA_OUT_F32 is set). */
+enum fa_dtype {
+    FA_F16 = 1,  /* IEEE binary16 */
+    FA_BF16 = 2  /* bfloat16 */
+};
+
+/* OR into dtype: o is written as float32 instead of the input element type. */
+#define FA_OUT_F32 0x100
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID = 1,     /* a precondition above is violated */
+    FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. d = 96) */
+    FA_ERR_WORKSPACE = 3,   /* fa_decode workspace missing, misaligned or too small */
+    FA_ERR_HIP = 4          /* the HIP runtime reported an error (see fa_last_error) */
+};
+
+/*
+ * Prefill / general forward: O and LSE for B*H heads of Nq queries against
+ * Nkv keys.  `causal` non-zero applies the mask described above.  `scale`
+ * multiplies every dot product before the softmax (1/sqrt(d) for the
+ * textbook form).  See the file comment for layout, ownership and errors.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int Nq, int Nkv, int d, int causal, float scale, int dtype,
+           hipStream_t stream);
+
+/*
+ * Decode: one query per (b, h) against Nkv cached keys and values, all visible
+ * ("Flash Attention -- Module 12.3", section "Prefill vs Decode": T_q = 1
+ * against a long cache).  The key range is cut into `num_splits` chunks that
+ * are processed in parallel, each producing a partial softmax result, and the
+ * partials are then merged exactly by their LSE values -- the split-KV scheme
+ * of "FlashAttention 1-2-3 ...", section "Beyond FlashAttention: Future
+ * Directions and Alternatives" (parallelising over the KV length, then a
+ * reduction).  num_splits = 0 lets the library choose (fa_decode_num_splits);
+ * any positive value is clamped to [1, Nkv].  The result is within rounding of
+ * the definition for every split count.
+ *
+ * workspace: caller-owned device memory of at least
+ * fa_decode_workspace_size(B, H, Nkv, d, num_splits) bytes, 16-byte aligned,
+ * not overlapping any other argument.  Its contents on entry are ignored and
+ * on return are unspecified.  Calls that share a workspace must be ordered on
+ * one stream.  A missing, misaligned or short workspace returns
+ * FA_ERR_WORKSPACE.
+ */
+int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int Nkv, int d, float scale, int dtype, int num_splits,
+              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace fa_decode needs for these arguments (0 if they are invalid). */
+size_t fa_decode_workspace_size(int B, int H, int Nkv, int d, int num_splits);
+
+/* The split count fa_decode uses for num_splits = 0 (0 if the arguments are invalid). */
+int fa_decode_num_splits(int B, int H, int Nkv, int d);
+
+/* Static, human-readable name of a status code. */
+const char *fa_status_str(int status);
+
+/* The calling thread's message for its last non-OK return ("" if none). */
+const char *fa_last_error(void);
+
+/* FA355_VERSION of the loaded library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: symbols, status strings and host-side validation.
+
+Every call here is rejected (or sized) on the host before any HIP call, so
+these tests run on a machine with no GPU.  No call here launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_65_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+# fake device addresses: never dereferenced, because validation rejects every call
+A = 1 << 32
+B_ = 2 << 32
+C = 3 << 32
+O = 4 << 32
+L = 5 << 32
+W = 6 << 32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "fa_decode", "fa_decode_num_splits", "fa_decode_workspace_size", "fa_fwd",
+        "fa_last_error", "fa_status_str", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert hasattr(fa, name), f"binding lacks {name}"
+
+
+def test_version_and_status_strings():
+    assert fa.fa_version() == 1
+    assert [fa.fa_status_str(s) for s in range(5)] == [
+        "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP"]
+    assert fa.fa_status_str(99) == "FA_ERR_UNKNOWN"
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except fa.FaError as e:
+        return e.status, fa.fa_last_error()
+    return fa.FA_OK, ""
+
+
+def fwd(q=A, k=B_, v=C, o=O, lse=L, B=1, H=2, Nq=64, Nkv=64, d=128, causal=0, scale=0.125, dtype=fa.FA_F16):
+    return status_of(fa.fa_fwd, q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), fa.FA_ERR_INVALID, "non-NULL"),
+    (dict(o=None), fa.FA_ERR_INVALID, "non-NULL"),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED, "d=96"),
+    (dict(d=0), fa.FA_ERR_INVALID, "positive"),
+    (dict(dtype=3), fa.FA_ERR_INVALID, "dtype"),
+    (dict(dtype=fa.FA_F16 | 0x200), fa.FA_ERR_INVALID, "dtype"),
+    (dict(causal=1, Nq=65, Nkv=64), fa.FA_ERR_INVALID, "Nq <= Nkv"),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID, "finite"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID, "finite"),
+    (dict(Nkv=0), fa.FA_ERR_INVALID, "no keys"),
+    (dict(B=-1), fa.FA_ERR_INVALID, "negative"),
+    (dict(q=A + 8), fa.FA_ERR_INVALID, "aligned"),
+    (dict(lse=L + 2), fa.FA_ERR_INVALID, "aligned"),
+    (dict(o=A), fa.FA_ERR_INVALID, "o overlaps q"),
+    (dict(o=A + 1024 * 16), fa.FA_ERR_INVALID, "o overlaps q"),
+    (dict(lse=C), fa.FA_ERR_INVALID, "lse overlaps v"),
+    (dict(lse=O + 16), fa.FA_ERR_INVALID, "lse overlaps o"),
+    (dict(B=1 << 20, H=1 << 20, Nq=1 << 20, Nkv=1 << 20), fa.FA_ERR_INVALID, "2^62"),
+])
+def test_fwd_rejects(kw, status, needle):
+    got, msg = fwd(**kw)
+    assert got == status, (got, msg)
+    assert needle in msg, msg
+
+
+def test_fwd_empty_is_noop():
+    # nothing to compute: OK without touching the (null) pointers or the GPU
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, Nq=0)[0] == fa.FA_OK
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, B=0)[0] == fa.FA_OK
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, H=0)[0] == fa.FA_OK
+
+
+def dec(q=A, k=B_, v=C, o=O, lse=L, B=2, H=2, Nkv=1000, d=128, scale=0.1, dtype=fa.FA_F16, splits=0,
+        ws=W, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = fa.fa_decode_workspace_size(B, H, Nkv, d, splits)
+    return status_of(fa.fa_decode, q, k, v, o, lse, B, H, Nkv, d, scale, dtype, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED, "d=80"),
+    (dict(Nkv=0), fa.FA_ERR_INVALID, "no keys"),
+    (dict(splits=-1), fa.FA_ERR_INVALID, "num_splits"),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE, "workspace"),
+    (dict(ws=W + 4), fa.FA_ERR_WORKSPACE, "aligned"),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE, "hold"),
+    (dict(ws=B_), fa.FA_ERR_WORKSPACE, "workspace overlaps k"),
+    (dict(v=None), fa.FA_ERR_INVALID, "non-NULL"),
+    (dict(dtype=0), fa.FA_ERR_INVALID, "dtype"),
+])
+def test_decode_rejects(kw, status, needle):
+    got, msg = dec(**kw)
+    assert got == status, (got, msg)
+    assert needle in msg, msg
+
+
+def test_decode_sizes():
+    # workspace = B*H*splits*(d+1) fp32; splits clamp to Nkv and never leave a split empty
+    assert fa.fa_decode_workspace_size(2, 3, 1000, 128, 4) == 2 * 3 * 4 * 129 * 4
+    assert fa.fa_decode_workspace_size(1, 1, 5, 64, 16) == 1 * 1 * 5 * 65 * 4
+    # 10 keys in 4 requested splits: chunks of 3 -> 4 splits (3,3,3,1)
+    assert fa.fa_decode_workspace_size(1, 1, 10, 64, 4) == 4 * 65 * 4
+    # 10 keys in 6 requested splits: chunks of 2 -> 5 splits
+    assert fa.fa_decode_workspace_size(1, 1, 10, 64, 6) == 5 * 65 * 4
+    assert fa.fa_decode_workspace_size(1, 1, 0, 64, 0) == 0
+    assert fa.fa_decode_workspace_size(1, 1, 10, 96, 0) == 0
+    s = fa.fa_decode_num_splits(16, 32, 32768, 128)
+    assert 1 <= s <= 256
+    assert fa.fa_decode_workspace_size(16, 32, 32768, 128, 0) == 16 * 32 * s * 129 * 4
+    assert fa.fa_decode_num_splits(1, 1, 1, 128) == 1
+    assert dec(B=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0)[0] == fa.FA_OK
+
+
+def test_last_error_is_per_thread():
+    import threading
+    fwd(d=96)
+    seen = {}
+
+    def other():
+        seen["msg"] = fa.fa_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "d=96" in fa.fa_last_error()
