@@ -100,19 +100,30 @@ template <> inline constexpr uint32_t kOnePair<__bf16> = 0x3F803F80u;
 // 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// {x of this lane, x of lane ^ 32} in some order (v_permlane32_swap).  Any
-// symmetric combination (max, sum) of the pair is the same in both lanes.
+// {x of this lane, x of lane ^ 32} in some order (v_permlane32_swap moves
+// lanes 32..63 of its first operand and lanes 0..31 of its second across the
+// halves).  Any symmetric combination (max, sum) of the pair is the same in
+// both lanes.  The two results are copied to scalars before the bit cast:
+// clang lowers __builtin_bit_cast of a vector element as a read of element 0.
+__device__ __forceinline__ void pair_with_other_half(float x, float &a, float &b)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
 __device__ __forceinline__ float max_with_other_half(float x)
 {
-    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                              __builtin_bit_cast(uint32_t, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    float a, b;
+    pair_with_other_half(x, a, b);
+    return fmaxf(a, b);
 }
 __device__ __forceinline__ float sum_with_other_half(float x)
 {
-    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                              __builtin_bit_cast(uint32_t, x), false, false);
-    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+    float a, b;
+    pair_with_other_half(x, a, b);
+    return a + b;
 }
 
 // DPP lane exchanges inside a 16-lane row.

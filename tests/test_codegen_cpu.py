@@ -1,0 +1,49 @@
+"""Checks on the code hipcc emits for gfx950 (CPU only: cross-compilation, no GPU).
+
+The half-wave exchange in the prefill kernel relies on both results of the
+permlane32 swap; an earlier form of the helper (a bit cast applied directly to
+a vector element) was lowered by clang as two reads of the first result.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "exact_io_aware_65_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None,
+                                reason="hipcc not available")
+
+
+def device_ir(src, tmp_path):
+    out = tmp_path / "k.ll"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                    "-I", CSRC, "-x", "hip", "-S", "--cuda-device-only", "-emit-llvm",
+                    os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
+    return out.read_text()
+
+
+def test_permlane_swap_uses_both_results(tmp_path):
+    ir = device_ir("fa_fwd.hip", tmp_path)
+    calls = re.findall(r"(%\d+) = tail call \{ i32, i32 \} @llvm\.amdgcn\.permlane32\.swap", ir)
+    assert calls, "prefill kernel no longer uses permlane32.swap"
+    for v in calls:
+        assert re.search(rf"extractvalue \{{ i32, i32 \}} {v}, 0", ir), v
+        assert re.search(rf"extractvalue \{{ i32, i32 \}} {v}, 1", ir), f"second result of {v} unused"
+
+
+def test_no_packed_fp32_arithmetic(tmp_path):
+    # packed fp32 add/mul/fma are kept out of the kernels
+    asm = tmp_path / "k.s"
+    for src in ("fa_fwd.hip", "fa_decode.hip"):
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+                        "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip",
+                        "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", str(asm)],
+                       check=True, capture_output=True)
+        text = asm.read_text()
+        for op in ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32"):
+            assert op not in text, f"{op} in {src}"
