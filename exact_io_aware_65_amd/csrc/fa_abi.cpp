@@ -133,6 +133,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     if (causal && Nq > Nkv)
         return fail(FA_ERR_INVALID, "%s: causal attention needs Nq <= Nkv (got %d > %d)", fn, Nq, Nkv);
     if ((rc = check_tensors(fn, q, k, v, o, lse, B, H, Nq, Nkv, d, out_f32))) return rc;
+    if (static_cast<unsigned long long>(Nkv) * d * 2 > 0xffffffffULL ||
+        static_cast<unsigned long long>(Nq) * d * (out_f32 ? 4 : 2) > 0xffffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: one head of q, k, v or o exceeds 4 GiB", fn);
     const int rows = fa355::fwd_rows_per_block(d);
     const long long blocks = static_cast<long long>(B) * H * ((Nq + rows - 1) / rows);
     if (blocks > 0x7fffffffLL)
@@ -182,6 +185,8 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     if (Nkv == 0) return fail(FA_ERR_INVALID, "%s: Nkv=0: attention over no keys is undefined", fn);
     if ((rc = check_tensors(fn, q, k, v, o, lse, B, H, 1, Nkv, d, out_f32))) return rc;
 
+    if (static_cast<unsigned long long>(Nkv) * d * 2 > 0xffffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: one head of k or v exceeds 4 GiB", fn);
     int splits, chunk;
     resolve_splits(B, H, Nkv, d, num_splits, &splits, &chunk);
     const long long blocks = static_cast<long long>(B) * H * splits;

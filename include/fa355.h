@@ -65,7 +65,9 @@
  *   - B, H, Nq >= 0 (a zero makes the call a no-op returning FA_OK);
  *     Nkv >= 1 whenever there is work (attention over no keys is undefined);
  *   - causal requires Nq <= Nkv, so every row sees at least one key;
- *   - B*H*N*d fits in 2^62 elements.
+ *   - B*H*N*d fits in 2^62 elements, and one head of q, k, v or o is
+ *     smaller than 4 GiB (FA_ERR_UNSUPPORTED otherwise: the kernels address a
+ *     head through 32-bit range-checked buffer offsets).
  */
 #ifndef FA355_H
 #define FA355_H

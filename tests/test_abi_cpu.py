@@ -80,6 +80,7 @@ def fwd(q=A, k=B_, v=C, o=O, lse=L, B=1, H=2, Nq=64, Nkv=64, d=128, causal=0, sc
     (dict(lse=C), fa.FA_ERR_INVALID, "lse overlaps v"),
     (dict(lse=O + 16), fa.FA_ERR_INVALID, "lse overlaps o"),
     (dict(B=1 << 20, H=1 << 20, Nq=1 << 20, Nkv=1 << 20), fa.FA_ERR_INVALID, "2^62"),
+    (dict(B=1, H=1, Nq=64, Nkv=1 << 24, o=A + (1 << 31)), fa.FA_ERR_UNSUPPORTED, "4 GiB"),
 ])
 def test_fwd_rejects(kw, status, needle):
     got, msg = fwd(**kw)
