@@ -39,8 +39,10 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
 PREFILL = "prefill_8k_d128"
 DECODE = "decode_32k_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-KERNEL_SOURCES = ["exact_io_aware_65_amd/csrc/fa_fwd.hip", "exact_io_aware_65_amd/csrc/fa_decode.hip",
-                  "exact_io_aware_65_amd/csrc/fa_device.hpp"]
+KERNEL_SOURCES = {
+    "prefill": ["exact_io_aware_65_amd/csrc/fa_fwd.hip", "exact_io_aware_65_amd/csrc/fa_device.hpp"],
+    "decode": ["exact_io_aware_65_amd/csrc/fa_decode.hip", "exact_io_aware_65_amd/csrc/fa_device.hpp"],
+}
 
 
 # ---------------------------------------------------------------------------
@@ -62,24 +64,37 @@ def score_matrix_bytes(n, elt=2):
     return n * n * elt
 
 
-def kernel_source_digest():
+def kernel_source_digest(kernel):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernel sources."""
+def measured_traffic(kernel):
+    """HBM bytes per launch from rocprofv3 counters, if they were taken on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.loads(f.read().split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
-    if rec.get("kernel_source_digest") != kernel_source_digest():
+    if rec.get(f"{kernel}_digest") != kernel_source_digest(kernel):
         return None
-    return rec
+    return rec.get(f"{kernel}_bytes")
+
+
+def calibrate_copy():
+    """A plain device copy of 1 GiB, three times: the reference FETCH_SIZE / WRITE_SIZE are read on it."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copied_bytes": n, "times": 3}))
 
 
 # ---------------------------------------------------------------------------
@@ -114,7 +129,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = library choice)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="time only one half of the step (for profiling; the default is the whole path)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         if int(os.environ.get("RANK", "0")) == 0:
             print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -134,31 +156,38 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     pw, dw = fi.WORKLOADS[PREFILL], fi.WORKLOADS[DECODE]
 
-    log(f"generating {PREFILL}")
-    px = fi.make_inputs(pw)
-    pq, pk, pv = (fi.bits_to_torch(px[t], pw.dtype).to(dev) for t in "qkv")
-    log(f"generating {DECODE}")
-    dx = fi.make_inputs(dw)
-    dq, dk, dv = (fi.bits_to_torch(dx[t], dw.dtype).to(dev) for t in "qkv")
-    dx = None  # decode inputs are not needed on the host any more
-
-    po = torch.empty_like(pq)
-    plse = torch.empty((pw.B, pw.H, pw.Nq), dtype=torch.float32, device=dev)
-    do = torch.empty_like(dq)
-    dlse = torch.empty((dw.B, dw.H), dtype=torch.float32, device=dev)
+    run_prefill = args.only in ("all", "prefill")
+    run_decode = args.only in ("all", "decode")
+    px = None
+    if run_prefill or not args.no_cpu_baseline:
+        log(f"generating {PREFILL}")
+        px = fi.make_inputs(pw)
+    if run_prefill:
+        pq, pk, pv = (fi.bits_to_torch(px[t], pw.dtype).to(dev) for t in "qkv")
+        po = torch.empty_like(pq)
+        plse = torch.empty((pw.B, pw.H, pw.Nq), dtype=torch.float32, device=dev)
     ws_bytes = fa.fa_decode_workspace_size(dw.B, dw.H, dw.Nkv, dw.d, args.num_splits)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     splits = fa.fa_decode_num_splits(dw.B, dw.H, dw.Nkv, dw.d) if args.num_splits == 0 else \
         ws_bytes // (dw.B * dw.H * (dw.d + 1) * 4)
+    if run_decode:
+        log(f"generating {DECODE}")
+        dx = fi.make_inputs(dw)
+        dq, dk, dv = (fi.bits_to_torch(dx[t], dw.dtype).to(dev) for t in "qkv")
+        dx = None  # decode inputs are not needed on the host any more
+        do = torch.empty_like(dq)
+        dlse = torch.empty((dw.B, dw.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
     def step(ev):
         ev[0].record(stream)
-        fa.fa_fwd(pq, pk, pv, po, plse, pw.B, pw.H, pw.Nq, pw.Nkv, pw.d, pw.causal, pw.scale, fa.FA_F16, sp)
+        if run_prefill:
+            fa.fa_fwd(pq, pk, pv, po, plse, pw.B, pw.H, pw.Nq, pw.Nkv, pw.d, pw.causal, pw.scale, fa.FA_F16, sp)
         ev[1].record(stream)
-        fa.fa_decode(dq, dk, dv, do, dlse, dw.B, dw.H, dw.Nkv, dw.d, dw.scale, fa.FA_F16, args.num_splits,
-                     ws, ws_bytes, sp)
+        if run_decode:
+            fa.fa_decode(dq, dk, dv, do, dlse, dw.B, dw.H, dw.Nkv, dw.d, dw.scale, fa.FA_F16, args.num_splits,
+                         ws, ws_bytes, sp)
         ev[2].record(stream)
 
     def events():
@@ -184,14 +213,13 @@ def main():
     d_bytes = algorithmic_bytes(dw.B, dw.H, 1, dw.Nkv, dw.d)
     fwd_mean = statistics.fmean(fwd_ms)
     dec_mean = statistics.fmean(dec_ms)
-    tflops = p_flops / (fwd_mean * 1e-3) / 1e12
-    gbs = d_bytes / (dec_mean * 1e-3) / 1e9
+    tflops = p_flops / (fwd_mean * 1e-3) / 1e12 if run_prefill else 0.0
+    gbs = d_bytes / (dec_mean * 1e-3) / 1e9 if run_decode else 0.0
 
     def pct(xs, q):
         xs = sorted(xs)
         return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
 
-    traffic = measured_traffic()
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -219,7 +247,7 @@ def main():
             "peak": PEAK_MFMA_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4),
-            "traffic": traffic["prefill_bytes"] if traffic else None,
+            "traffic": measured_traffic("prefill"),
         },
         "roofline_decode": {
             "kernel": "decode_split_kernel<128, f16> + decode_combine_kernel",
@@ -228,7 +256,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": traffic["decode_bytes"] if traffic else None,
+            "traffic": measured_traffic("decode"),
         },
         "prefill": {"ms_mean": round(fwd_mean, 4), "ms_p10": round(pct(fwd_ms, 0.1), 4),
                     "ms_p50": round(pct(fwd_ms, 0.5), 4), "ms_p90": round(pct(fwd_ms, 0.9), 4),
@@ -239,6 +267,8 @@ def main():
         "gpu": {"name": props.name, "cus": props.multi_processor_count,
                 "arch": getattr(props, "gcnArchName", "")},
     }
+    if args.only != "all":
+        result["partial_step"] = args.only
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(pw, px)
