@@ -5,7 +5,7 @@
 // inner ("FlashAttention 1-2-3: The IO-Aware Revolution in LLM Inference",
 // section "FlashAttention-2: Reducing Non-Matmul Overhead and Causal
 // Efficiency").  Each K/V tile is copied once from HBM/L2 straight into LDS
-// (global_load_lds, no register staging) while the previous tile is being
+// (buffer_load ... lds, no register staging) while earlier tiles are being
 // consumed -- the double buffering of that page's section "FlashAttention-3"
 // done with the gfx950 direct-to-LDS load.  The score tile lives only in
 // registers and is consumed by an online softmax (running max m, running sum
@@ -27,12 +27,27 @@
 // V stays [key][dim] in LDS; its transposed operand comes from two
 // ds_read_b64_tr_b16 reads per MFMA.
 //
-// Softmax work per score: one max (three-input), one FMA (scale folded in,
+// Software pipeline (per wave, per key tile j):
+//   phase 1: the 16 MFMAs of S_{j+1} = K_{j+1} Q^T are issued while the VALU
+//            turns S_j into probabilities (FMA + exp2, row sum, pack to 16 bits);
+//   phase 2: the 16 MFMAs of O += V_j P_j are issued while the VALU takes the
+//            row maximum of S_{j+1}.
+// A wave's own VALU work runs beside its MFMAs when the two are independent,
+// which is what this ordering gives the scheduler.  K therefore runs one tile
+// ahead of V in the LDS ring.
+//
+// LDS layout: rows of d 16-bit elements (row stride 2d bytes) with the 16-byte
+// chunks of each row permuted by an XOR with a function of the row.  gfx950
+// serves a ds_read_b128 in groups of 16 consecutive lanes and a ds_read_b64 /
+// ds_read_b64_tr_b16 in groups of 32, each group over 64 four-byte banks; the
+// two permutations below make every K and V operand read conflict-free.
+//
+// Softmax work per score: half a three-input max, one FMA (scale folded in,
 // base-2 domain), one exp2, one add for the fp32 row sum and half a pack to
-// 16 bits.  The accumulator is rescaled only when some row's
-// maximum grows by more than 2^8 over the value in use; otherwise the stale
-// maximum is kept, which bounds every probability by 2^8 and leaves the final
-// O = acc / l exact, because numerator and denominator share the factor.
+// 16 bits.  The accumulator is rescaled only when some row's maximum grows by
+// more than 2^8 over the value in use; otherwise the stale maximum is kept,
+// which bounds every probability by 2^8 and leaves the final O = acc / l exact,
+// because numerator and denominator share the factor.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -44,6 +59,7 @@ namespace {
 constexpr int kBN = 64;                // keys per tile
 constexpr int kNW = 4;                 // waves per workgroup (32 query rows each)
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest probability kept without rescaling
+constexpr float kMinC = 1e-30f;        // lower bound of the exponent scale (see launch)
 
 struct FwdParams {
     const void *q, *k, *v;
@@ -51,20 +67,31 @@ struct FwdParams {
     float *lse;
     int Nq, Nkv;
     int n_bh, n_qt;
-    float c;         // |scale| * log2(e): scores are kept in the base-2 domain
+    float c;         // max(|scale| * log2(e), kMinC): scores are kept in the base-2 domain
     uint32_t qsign;  // 0x80008000 when scale < 0: Q is negated as it is loaded
 };
+
+template <int N> using IC = std::integral_constant<int, N>;
 
 // The MFMA row that lane l % 32 feeds is key swap23(l % 32) of the sub-tile
 // (bits 2 and 3 exchanged); see the file comment.
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-// XOR swizzles of the 16-byte chunk index of a row in LDS.  K: eight lanes
-// reading one chunk column of rows swap23(0..7) hit eight bank groups.  V:
-// the 16 lanes of a transposed read touch 4 consecutive rows x 2 adjacent
-// chunks, which this spreads over all 32 banks.
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int vswz(int row) { return (row & 3) << 1; }
+// XOR permutations of the 16-byte chunk index within a row, as functions of
+// the row.  K is read as 16-byte runs by 16 lanes holding rows swap23(0..15)
+// (+ a multiple of 16) at one logical chunk: the permutation must send those
+// 16 rows to 16 distinct 16-byte bank groups.  V is read transposed: 32 lanes
+// cover 4 consecutive rows (starting at a multiple of 4) x 64 bytes, so the 4
+// rows must land in 4 distinct 64-byte bank segments.  For d = 64 two rows
+// share one 256-byte bank line, hence the extra shift by one row bit.
+template <int D> __device__ __forceinline__ int kswz(int row)
+{
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int vswz(int row)
+{
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 
 template <int D, typename T, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -75,11 +102,13 @@ void fwd_kernel(FwdParams p)
     constexpr int TILE = BN * DC;        // chunks per K (or V) tile
     constexpr int LOADS = TILE / NT;     // direct loads per thread per tensor per tile
     constexpr int ROWB = D * 2;          // bytes per row
+    constexpr int KS = D / 16;           // k-steps of the first product
+    constexpr int DT = D / 32;           // 32-dim blocks of the output
     static_assert(TILE % NT == 0 && LOADS >= 1, "tile must split evenly over the threads");
     using V8 = typename Vec<T>::v8;
 
-    __shared__ u32x4 sk0[TILE], sk1[TILE];  // K tiles [key][dim], chunk-swizzled (two stages)
-    __shared__ u32x4 sv0[TILE], sv1[TILE];  // V tiles [key][dim], chunk-swizzled
+    __shared__ u32x4 sk[2][TILE];  // K tiles [key][dim], chunk-permuted (two stages)
+    __shared__ u32x4 sv[2][TILE];  // V tiles [key][dim], chunk-permuted (two stages)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
@@ -95,7 +124,7 @@ void fwd_kernel(FwdParams p)
     const int off = p.Nkv - p.Nq;  // causal: row i sees keys j <= i + off
     int kend = p.Nkv;
     if constexpr (CAUSAL) kend = min(p.Nkv, min(q0 + BM, p.Nq) + off);
-    const int nkb = (kend + BN - 1) / BN;
+    const int nkb = (kend + BN - 1) / BN;  // >= 1: every row sees key 0
 
     // Per-head buffer descriptors: reads past a head's last row return zeros,
     // which fills the ragged end of the last tile (those keys are masked) and
@@ -108,181 +137,244 @@ void fwd_kernel(FwdParams p)
 
     // Q operand, loaded once: lane (c, h) holds query wq0 + c, dims 16 s + 8 h .. + 7.
     const int qrow = wq0 + c;
-    V8 qf[D / 16];
+    V8 qf[KS];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+    for (int s = 0; s < KS; ++s) {
         const u32x4 x = buffer_load16(rq, qrow * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.qsign;
         qf[s] = as<V8>(x);
     }
 
     // Direct loads: the wave's i-th load fills LDS chunks [(wave*LOADS + i)*64, +64),
-    // lane by lane; the lane fetches whichever global chunk the swizzle puts there.
-    uint32_t koff[LOADS], voff[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
+    // lane by lane; the lane fetches whichever global chunk the permutation puts
+    // there.  The offsets are recomputed at each issue (a few VALU ops per tile)
+    // rather than held in registers across the loop.
+    auto ld_off = [&](int i, bool is_k) {
         const int pch = (wave * LOADS + i) * 64 + lane;
         const int row = pch / DC, col = pch % DC;
-        koff[i] = row * ROWB + (col ^ kswz(row)) * 16;
-        voff[i] = row * ROWB + (col ^ vswz(row)) * 16;
-    }
-    auto issue = [&](auto stage_, int kb) {
-        constexpr int S = decltype(stage_)::value;
-        u32x4 *dk = S ? sk1 : sk0;
-        u32x4 *dv = S ? sv1 : sv0;
+        return static_cast<uint32_t>(row * ROWB + ((col ^ (is_k ? kswz<D>(row) : vswz<D>(row))) << 4));
+    };
+    auto issue_k = [&](auto st, int kb) {
         const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            buffer_to_lds16(rk, koff[i], tile, dk + (wave * LOADS + i) * 64);
-            buffer_to_lds16(rv, voff[i], tile, dv + (wave * LOADS + i) * 64);
-        }
+        for (int i = 0; i < LOADS; ++i)
+            buffer_to_lds16(rk, ld_off(i, true), tile, &sk[decltype(st)::value][(wave * LOADS + i) * 64]);
+    };
+    auto issue_v = [&](auto st, int kb) {
+        const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            buffer_to_lds16(rv, ld_off(i, false), tile, &sv[decltype(st)::value][(wave * LOADS + i) * 64]);
     };
 
-    // LDS byte addresses of this lane's MFMA operands, as a few bases plus
-    // compile-time offsets.  K operand (kk, s): row 32 kk + swap23(c), chunk
-    // (2 s + h) ^ kswz(row); s and s + 4 differ by 8 chunks, kk by 32 rows.
-    uint32_t ka[4];
+    // LDS byte offsets of this lane's MFMA operands within a tile.
+    // K operand (kk, s): row 32 kk + swap23(c), logical chunk 2 s + h.  The
+    // permutation is an XOR on the chunk index, so step s is the step-0 offset
+    // with bits 5.. of the in-row byte offset XOR-ed by s; kk adds 32 rows,
+    // which leaves the permutation unchanged.
+    uint32_t ka0;
     {
         const int krow = swap23(c);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ka[s] = krow * ROWB + (((2 * s + h) ^ kswz(krow)) << 4);
+        ka0 = krow * ROWB + ((h ^ kswz<D>(krow)) << 4);
     }
-    // V^T operand: lane 16 g + 4 j + q addresses key 8 (g / 2) + j (+4, +16 u,
-    // +32 kk) and dims 32 dt + 16 (g % 2) + 4 q; with the swizzle the chunk is
-    // 4 (dt ^ (j / 2)) + ((2 (g % 2) + q / 2) ^ 2 (j % 2)), so dt = 0, 1 need
-    // their own base and dt = 2, 3 add 128 bytes.
-    uint32_t va[2];
+    // V^T operand (dt, kk, u, half): lane 16 g + 4 j + q addresses key
+    // 32 kk + 16 u + 8 (g / 2) + j + 4 half and dims 32 dt + 16 (g % 2) + 4 q .. + 3,
+    // i.e. logical chunk 4 dt + 2 (g % 2) + q / 2, byte 8 (q % 2) within it.
+    // dt enters as an XOR on bits 6.. of the in-row offset; kk, u and half move
+    // the row by multiples of 4, which leaves the permutation unchanged, so
+    // they are compile-time offsets.
+    uint32_t va0;
     {
-        const int tg = lane >> 4, tj = (lane >> 2) & 3, tq = lane & 3;
-        const int base = (8 * (tg >> 1) + tj) * ROWB + ((tq & 1) << 3);
-        const int y = (2 * (tg & 1) + (tq >> 1)) ^ (2 * (tj & 1));
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) va[dt] = base + ((4 * (dt ^ (tj >> 1)) + y) << 4);
+        const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+        const int row = 8 * (g >> 1) + j;
+        va0 = row * ROWB + (((2 * (g & 1) + (q >> 1)) ^ vswz<D>(row)) << 4) + ((q & 1) << 3);
     }
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[DT];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
     float m_run = -INFINITY;  // row max (base-2 scaled) the probabilities are taken against
     float l_run = 0.f;        // running sum over this lane's half of the keys
+    const float cs = p.c;
 
-    auto compute = [&](auto stage_, int kv0) {
-        constexpr int S = decltype(stage_)::value;
-        const char *SK = reinterpret_cast<const char *>(S ? sk1 : sk0);
-        const char *SV = reinterpret_cast<const char *>(S ? sv1 : sv0);
-
-        // S^T = K Q^T for the two 32-key sub-tiles
-        f32x16 sacc[BN / 32];
+    // S^T = K Q^T for the K tile in stage st (two 32-key sub-tiles).
+    auto scores = [&](auto st, f32x16 (&sn)[2]) {
+        const char *SK = reinterpret_cast<const char *>(sk[decltype(st)::value]);
 #pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[kk][e] = 0.f;
+            for (int e = 0; e < 16; ++e) sn[kk][e] = 0.f;
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(SK + ka[s & 3] + (s >> 2) * 128 + kk * 32 * ROWB);
-                sacc[kk] = mfma32(as<V8>(x), qf[s], sacc[kk]);
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ (s << 5)) + kk * 32 * ROWB);
+                sn[kk] = mfma32(as<V8>(x), qf[s], sn[kk]);
             }
-        }
+    };
 
-        // causal diagonal / ragged end: invisible keys get -inf
-        const bool need_mask = (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
-        if (need_mask) {
+    // causal diagonal / ragged end: invisible keys get -inf
+    auto needs_mask = [&](int kv0) { return (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off); };
+    auto mask = [&](f32x16 (&sn)[2], int kv0) {
 #pragma unroll
-            for (int kk = 0; kk < BN / 32; ++kk)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = kv0 + 32 * kk + 16 * (e >> 3) + 8 * h + (e & 7);
-                    if (key >= p.Nkv || (CAUSAL && key > qrow + off)) sacc[kk][e] = -INFINITY;
-                }
-        }
+            for (int e = 0; e < 16; ++e) {
+                const int key = kv0 + 32 * kk + 16 * (e >> 3) + 8 * h + (e & 7);
+                if (key >= p.Nkv || (CAUSAL && key > qrow + off)) sn[kk][e] = -INFINITY;
+            }
+    };
 
-        // block max (raw scores; c >= 0), then the lazy rescale
-        float mx = sacc[0][0];
+    // Row maximum of a score tile, scaled to the base-2 domain (c > 0); two
+    // chains of three-input maxima.
+    auto rowmax = [&](const f32x16 (&sn)[2]) {
+        float m0 = fmaxf(sn[0][0], sn[0][1]), m1 = fmaxf(sn[1][0], sn[1][1]);
 #pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kk][e]);
-        mx = max_with_other_half(mx);
-        const float m_blk = mx == -INFINITY ? -INFINITY : mx * p.c;
+        for (int e = 2; e < 16; e += 2) {
+            m0 = fmaxf(fmaxf(m0, sn[0][e]), sn[0][e + 1]);
+            m1 = fmaxf(fmaxf(m1, sn[1][e]), sn[1][e + 1]);
+        }
+        return max_with_other_half(fmaxf(m0, m1)) * cs;
+    };
+
+    // Lazy rescale: only when some row's block max exceeds the max in use by
+    // more than the slack (a wave-uniform branch).
+    auto rescale = [&](float m_blk) {
         if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kRescaleSlack)) {
             const float m_new = fmaxf(m_run, m_blk);
             const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
             l_run *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
             m_run = m_new;
         }
-        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    };
 
-        // p = 2^(c s - m); the row sum is taken in fp32 before rounding P
-        float rs = 0.f;
-        if (need_mask) {
+    // p = 2^(c s - m) (exactly 0 for masked keys) and P in the storage type:
+    // operand (kk, u) holds keys 32 kk + 16 u + 8 h .. + 7.  The row sum:
+    //  - fp16: the rounded P that the second product uses, summed in fp32 by
+    //    v_dot2 (rowsum_p, in phase 2); P's rounding error is at most 2^-11 of
+    //    each term, so the normalisation stays consistent with the numerator;
+    //  - bf16: the fp32 values before rounding (2^-9 per term would be too
+    //    coarse for the log-sum-exp).
+    constexpr bool kSumP = std::is_same<T, _Float16>::value;
+    auto softmax = [&](f32x16 (&sc)[2], V8 (&pf)[2][2]) {
+        const float neg_m = -m_run;  // finite: every row sees key 0 in the first tile
+        float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < BN / 32; ++kk)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float x = sacc[kk][e];
-                    sacc[kk][e] = x == -INFINITY ? 0.f : fast_exp2(fmaf(x, p.c, neg_m));
-                    rs += sacc[kk][e];
-                }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < BN / 32; ++kk)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    sacc[kk][e] = fast_exp2(fmaf(sacc[kk][e], p.c, neg_m));
-                    rs += sacc[kk][e];
-                }
-        }
-        l_run += rs;
-
-        // P to the storage type: operand (kk, u) holds keys 32 kk + 16 u + 8 h .. + 7.
-        V8 pf[BN / 32][2];
-#pragma unroll
-        for (int kk = 0; kk < BN / 32; ++kk)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 u32x4 w;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) w[j] = pack2<T>(sacc[kk][8 * u + 2 * j], sacc[kk][8 * u + 2 * j + 1]);
+                for (int j = 0; j < 4; ++j) {
+                    const float a = fast_exp2(fmaf(sc[kk][8 * u + 2 * j], cs, neg_m));
+                    const float b = fast_exp2(fmaf(sc[kk][8 * u + 2 * j + 1], cs, neg_m));
+                    if constexpr (!kSumP) {
+                        rs0 += a;
+                        rs1 += b;
+                    }
+                    w[j] = pack2<T>(a, b);
+                }
                 pf[kk][u] = as<V8>(w);
             }
-
-        // O^T += V^T P^T (two transposed reads per operand: keys +0..3 and +4..7)
+        if constexpr (!kSumP) {
+            l_run += rs0 + rs1;
+            asm volatile("" : "+v"(l_run));  // keep the adds beside the exps
+        }
+    };
+    auto rowsum_p = [&](const V8 (&pf)[2][2]) {
+        if constexpr (kSumP) {
+            const uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in binary16
+            float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-            for (int kk = 0; kk < BN / 32; ++kk)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const char *pa = SV + va[dt & 1] + (dt >> 1) * 128 + (32 * kk + 16 * u) * ROWB;
-                    const u32x2 lo = lds_read_tr16(pa);
-                    const u32x2 hi = lds_read_tr16(pa + 4 * ROWB);  // rows + 4: same swizzle
-                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                    oacc[dt] = mfma32(as<V8>(a), pf[kk][u], oacc[dt]);
+                    const u32x4 w = __builtin_bit_cast(u32x4, pf[kk][u]);
+                    r0 = dot2<T>(w[0], ones, r0);
+                    r1 = dot2<T>(w[1], ones, r1);
+                    r0 = dot2<T>(w[2], ones, r0);
+                    r1 = dot2<T>(w[3], ones, r1);
                 }
+            l_run += r0 + r1;
         }
     };
 
-    auto step = [&](auto stage_, int kb) {
-        constexpr int S = decltype(stage_)::value;
-        if (kb + 1 < nkb) issue(std::integral_constant<int, S ^ 1>{}, kb + 1);
-        const int kv0 = kb * BN;
-        const bool active = wq0 < p.Nq && (!CAUSAL || kv0 <= wq0 + 31 + off);
-        if (active) compute(stage_, kv0);
+    // O^T += V^T P^T for the V tile in stage st (two transposed reads per operand).
+    auto pv = [&](auto st, const V8 (&pf)[2][2]) {
+        const char *SV = reinterpret_cast<const char *>(sv[decltype(st)::value]);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const char *pa = SV + (va0 ^ (dt << 6)) + (32 * kk + 16 * u) * ROWB;
+                    const u32x2 lo = lds_read_tr16(pa);
+                    const u32x2 hi = lds_read_tr16(pa + 4 * ROWB);
+                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                    oacc[dt] = mfma32(as<V8>(a), pf[kk][u], oacc[dt]);
+                }
+    };
+
+    // An empty asm statement that claims to read and rewrite P: the compiler
+    // must form P before it, in the same block as the score MFMAs.
+    auto pin = [](V8 (&pf)[2][2]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                u32x4 w = __builtin_bit_cast(u32x4, pf[kk][u]);
+                asm volatile("" : "+v"(w));
+                pf[kk][u] = as<V8>(w);
+            }
+    };
+
+    // One pipeline step for key tile kb (stage S = kb % 2): V_kb sits in
+    // sv[S], K_{kb+1} in sk[S ^ 1]; K_{kb+2} and V_{kb+1} are loaded meanwhile.
+    // The step is straight-line apart from the rare rescale and mask branches:
+    // on the last tile the scores of the (absent) next tile are still formed,
+    // from stale LDS contents, and never used.
+    f32x16 sa[2], sb[2];
+    V8 pf[2][2];
+    float mx;
+    auto step = [&](auto st, f32x16 (&sc)[2], f32x16 (&sn)[2], int kb) {
+        constexpr int S = decltype(st)::value;
+        if (kb + 2 < nkb) issue_k(IC<S>{}, kb + 2);
+        if (kb + 1 < nkb) issue_v(IC<S ^ 1>{}, kb + 1);
+        rescale(mx);
+        // phase 1: MFMAs of the next scores beside the softmax of the current ones
+        scores(IC<S ^ 1>{}, sn);
+        softmax(sc, pf);
+        pin(pf);  // P is formed here, not sunk past the mask branch
+        const int kv1 = (kb + 1) * BN;
+        if (kv1 < kend && needs_mask(kv1)) mask(sn, kv1);
+        // phase 2: MFMAs of O += V P beside the row max of the next scores
+        pv(IC<S>{}, pf);
+        rowsum_p(pf);
+        mx = rowmax(sn);
         wait_vmem();
         __syncthreads();
     };
 
-    if (nkb > 0) issue(std::integral_constant<int, 0>{}, 0);
+    // Prologue: K_0, V_0 and K_1 in flight, then S_0 and its row max.
+    issue_k(IC<0>{}, 0);
+    issue_v(IC<0>{}, 0);
+    if (nkb > 1) issue_k(IC<1>{}, 1);
     wait_vmem();
     __syncthreads();
+    scores(IC<0>{}, sa);
+    if (needs_mask(0)) mask(sa, 0);
+    mx = rowmax(sa);
+    __syncthreads();  // every wave is done with sk[0] before K_2 refills it
+
     for (int kb = 0; kb < nkb; kb += 2) {
-        step(std::integral_constant<int, 0>{}, kb);
-        if (kb + 1 < nkb) step(std::integral_constant<int, 1>{}, kb + 1);
+        step(IC<0>{}, sa, sb, kb);
+        if (kb + 1 < nkb) step(IC<1>{}, sb, sa, kb + 1);
     }
 
     // Epilogue: O = acc / l, LSE = ln 2 * (m + log2 l).
@@ -291,7 +383,7 @@ void fwd_kernel(FwdParams p)
         const float inv = 1.f / l_tot;
         const size_t orow = (static_cast<size_t>(bh) * p.Nq + qrow) * D;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d0 = 32 * dt + 8 * j + 4 * h;
@@ -304,10 +396,7 @@ void fwd_kernel(FwdParams p)
                         u32x2{pack2<T>(a0, a1), pack2<T>(a2, a3)};
                 }
             }
-        if (h == 0 && p.lse) {
-            const float m = m_run == -INFINITY ? 0.f : m_run;
-            p.lse[static_cast<size_t>(bh) * p.Nq + qrow] = (m + __builtin_amdgcn_logf(l_tot)) * kLn2;
-        }
+        if (h == 0 && p.lse) p.lse[static_cast<size_t>(bh) * p.Nq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
@@ -325,7 +414,11 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
     p.Nkv = a.Nkv;
     p.n_bh = a.B * a.H;
     p.n_qt = (a.Nq + BM - 1) / BM;
-    p.c = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
+    // A zero scale would make a masked score (-inf) times c a NaN; any c up to
+    // kMinC leaves every finite score's 2^(c s - m) equal to 1 in fp32, which
+    // is the uniform weighting a zero scale asks for.
+    const float c = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
+    p.c = c < kMinC ? kMinC : c;
     p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_qt));
     hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, OUT_F32>), grid, dim3(64 * kNW), 0, stream, p);
