@@ -23,7 +23,7 @@ ARCH = "gfx950"
 SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_abi.cpp"]
 
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     # keep hipcc from forming packed fp32 arithmetic on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

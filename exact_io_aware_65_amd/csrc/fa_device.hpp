@@ -118,6 +118,42 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, uint32
                                              0, 0);
 }
 
+// Buffer resource as four scalar words: base address, stride 0, byte range
+// and the same format word make_rsrc uses.  Every argument must be
+// wave-uniform.
+__device__ __forceinline__ u32x4 make_rsrc_words(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Buffer -> LDS copy of 16 bytes per lane, issued so that the compiler does
+// not track it: lane i's 16 bytes from byte offset voff + soff + IMM land at
+// lds_base + IMM + 16 * i (the instruction offset moves both addresses);
+// reads past the range write zeros.  The compiler would otherwise make every
+// later LDS read wait for the copy (it cannot tell which LDS bytes the copy
+// writes), which serialises a prefetch ring.  The caller waits with
+// wait_vmcnt<N>() before a barrier that publishes the data.  The LDS offset
+// of a shared-memory pointer is the low 32 bits of its flat address (the
+// aperture is 4 GiB aligned).
+template <int IMM = 0>
+__device__ __forceinline__ void dma_to_lds16(u32x4 rsrc, uint32_t voff, uint32_t soff, const void *lds_base)
+{
+    static_assert(IMM >= 0 && IMM < 4096, "12-bit instruction offset");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0), "n"(IMM)
+                 : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // 16-byte buffer load into registers (zeros when out of range).
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {

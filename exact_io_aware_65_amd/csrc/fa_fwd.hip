@@ -52,12 +52,12 @@
 #include "fa_internal.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace fa355 {
 namespace {
 
 constexpr int kBN = 64;                // keys per tile
-constexpr int kNW = 4;                 // waves per workgroup (32 query rows each)
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest probability kept without rescaling
 constexpr float kMinC = 1e-30f;        // lower bound of the exponent scale (see launch)
 
@@ -93,22 +93,44 @@ template <int D> __device__ __forceinline__ int vswz(int row)
     return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-template <int D, typename T, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Wait until at most n direct loads of this wave are in flight, n a multiple
+// of L in [0, K L] (s_waitcnt takes an immediate, so the few possible values
+// are dispatched).
+template <int L, int K> __device__ __forceinline__ void wait_loads(int n)
+{
+    if constexpr (K > 0) {
+        if (n >= K * L) {
+            wait_vmcnt<K * L>();
+            return;
+        }
+        wait_loads<L, K - 1>(n);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+constexpr int lcm2(int n) { return n % 2 ? 2 * n : n; }
+
+// NW waves of 32 query rows each (BM = 32 NW rows per workgroup) and a ring
+// of NS K/V stages.
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p)
 {
-    constexpr int BN = kBN, BM = 32 * kNW, NT = 64 * kNW;
+    constexpr int BN = kBN, BM = 32 * NW, NT = 64 * NW;
     constexpr int DC = D / 8;            // 16-byte chunks per row
     constexpr int TILE = BN * DC;        // chunks per K (or V) tile
     constexpr int LOADS = TILE / NT;     // direct loads per thread per tensor per tile
     constexpr int ROWB = D * 2;          // bytes per row
     constexpr int KS = D / 16;           // k-steps of the first product
     constexpr int DT = D / 32;           // 32-dim blocks of the output
-    static_assert(TILE % NT == 0 && LOADS >= 1, "tile must split evenly over the threads");
+    constexpr int U = lcm2(NS);          // steps per loop iteration (stage and score-set periods)
+    static_assert(NS >= 2 && TILE % NT == 0 && LOADS >= 1 && LOADS <= 4, "tile must split evenly over the threads");
+    static_assert(NS * TILE * 16 <= 65536, "stage offsets must fit the 16-bit LDS immediate");
     using V8 = typename Vec<T>::v8;
 
-    __shared__ u32x4 sk[2][TILE];  // K tiles [key][dim], chunk-permuted (two stages)
-    __shared__ u32x4 sv[2][TILE];  // V tiles [key][dim], chunk-permuted (two stages)
+    __shared__ u32x4 sk[NS][TILE];  // K tiles [key][dim], chunk-permuted
+    __shared__ u32x4 sv[NS][TILE];  // V tiles [key][dim], chunk-permuted
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
@@ -125,6 +147,12 @@ void fwd_kernel(FwdParams p)
     int kend = p.Nkv;
     if constexpr (CAUSAL) kend = min(p.Nkv, min(q0 + BM, p.Nq) + off);
     const int nkb = (kend + BN - 1) / BN;  // >= 1: every row sees key 0
+    // key tiles this wave's rows can see; 0 for a wave wholly past Nq
+    int nkw = 0;
+    if (wq0 < p.Nq) {
+        nkw = nkb;
+        if constexpr (CAUSAL) nkw = min(nkb, (min(wq0 + 31, p.Nq - 1) + off) / BN + 1);
+    }
 
     // Per-head buffer descriptors: reads past a head's last row return zeros,
     // which fills the ragged end of the last tile (those keys are masked) and
@@ -132,8 +160,8 @@ void fwd_kernel(FwdParams p)
     const size_t q_head = static_cast<size_t>(bh) * p.Nq * ROWB;
     const size_t kv_head = static_cast<size_t>(bh) * p.Nkv * ROWB;
     const auto rq = make_rsrc(static_cast<const char *>(p.q) + q_head, static_cast<uint32_t>(p.Nq) * ROWB);
-    const auto rk = make_rsrc(static_cast<const char *>(p.k) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
-    const auto rv = make_rsrc(static_cast<const char *>(p.v) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
+    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
+    const u32x4 rv = make_rsrc_words(static_cast<const char *>(p.v) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
 
     // Q operand, loaded once: lane (c, h) holds query wq0 + c, dims 16 s + 8 h .. + 7.
     const int qrow = wq0 + c;
@@ -144,26 +172,43 @@ void fwd_kernel(FwdParams p)
         qf[s] = as<V8>(x);
     }
 
-    // Direct loads: the wave's i-th load fills LDS chunks [(wave*LOADS + i)*64, +64),
-    // lane by lane; the lane fetches whichever global chunk the permutation puts
-    // there.  The offsets are recomputed at each issue (a few VALU ops per tile)
-    // rather than held in registers across the loop.
-    auto ld_off = [&](int i, bool is_k) {
-        const int pch = (wave * LOADS + i) * 64 + lane;
+    // Direct loads: the wave's i-th load of a tensor fills LDS chunks
+    // [(wave*LOADS + i)*64, +64) lane by lane; the lane fetches whichever
+    // global chunk the permutation puts there.  Load i sits 1024 bytes after
+    // load 0 both in memory and in LDS (the instruction offset), and only the
+    // K permutation changes with i, as an XOR on bits 6.. of the offset.
+    uint32_t koff0, voff0;
+    {
+        const int pch = wave * LOADS * 64 + lane;
         const int row = pch / DC, col = pch % DC;
-        return static_cast<uint32_t>(row * ROWB + ((col ^ (is_k ? kswz<D>(row) : vswz<D>(row))) << 4));
-    };
+        koff0 = row * ROWB + ((col ^ kswz<D>(row)) << 4);
+        voff0 = row * ROWB + ((col ^ vswz<D>(row)) << 4);
+    }
     auto issue_k = [&](auto st, int kb) {
         const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            buffer_to_lds16(rk, ld_off(i, true), tile, &sk[decltype(st)::value][(wave * LOADS + i) * 64]);
+        const u32x4 *dst = &sk[decltype(st)::value][wave * LOADS * 64];
+        dma_to_lds16<0>(rk, koff0, tile, dst);
+        if constexpr (LOADS > 1) dma_to_lds16<1024>(rk, koff0 ^ (1u << 6), tile, dst);
+        if constexpr (LOADS > 2) dma_to_lds16<2048>(rk, koff0 ^ (2u << 6), tile, dst);
+        if constexpr (LOADS > 3) dma_to_lds16<3072>(rk, koff0 ^ (3u << 6), tile, dst);
     };
     auto issue_v = [&](auto st, int kb) {
         const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
+        const u32x4 *dst = &sv[decltype(st)::value][wave * LOADS * 64];
+        dma_to_lds16<0>(rv, voff0, tile, dst);
+        if constexpr (LOADS > 1) dma_to_lds16<1024>(rv, voff0, tile, dst);
+        if constexpr (LOADS > 2) dma_to_lds16<2048>(rv, voff0, tile, dst);
+        if constexpr (LOADS > 3) dma_to_lds16<3072>(rv, voff0, tile, dst);
+    };
+    // Step j requests V_{j+NS-1} and K_{j+NS}; the prologue acts as steps
+    // 1 - NS .. -1.  At the end of step j, K_{j+2} and V_{j+1} must have
+    // landed, so the loads of steps j + 3 - NS .. j may stay in flight.
+    auto allowance = [&](int j) {
+        int n = 0;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i)
-            buffer_to_lds16(rv, ld_off(i, false), tile, &sv[decltype(st)::value][(wave * LOADS + i) * 64]);
+        for (int i = j + 3 - NS; i <= j; ++i)
+            if (i >= 1 - NS) n += LOADS * ((i + NS - 1 < nkb) + (i + NS < nkb));
+        return n;
     };
 
     // LDS byte offsets of this lane's MFMA operands within a tile.
@@ -303,6 +348,18 @@ void fwd_kernel(FwdParams p)
             l_run += r0 + r1;
         }
     };
+    // An empty asm statement that claims to read and rewrite P: the compiler
+    // must form P before it, in the same block as the score MFMAs.
+    auto pin = [](V8 (&pf)[2][2]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                u32x4 w = __builtin_bit_cast(u32x4, pf[kk][u]);
+                asm volatile("" : "+v"(w));
+                pf[kk][u] = as<V8>(w);
+            }
+    };
 
     // O^T += V^T P^T for the V tile in stage st (two transposed reads per operand).
     auto pv = [&](auto st, const V8 (&pf)[2][2]) {
@@ -321,60 +378,55 @@ void fwd_kernel(FwdParams p)
                 }
     };
 
-    // An empty asm statement that claims to read and rewrite P: the compiler
-    // must form P before it, in the same block as the score MFMAs.
-    auto pin = [](V8 (&pf)[2][2]) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                u32x4 w = __builtin_bit_cast(u32x4, pf[kk][u]);
-                asm volatile("" : "+v"(w));
-                pf[kk][u] = as<V8>(w);
-            }
-    };
-
-    // One pipeline step for key tile kb (stage S = kb % 2): V_kb sits in
-    // sv[S], K_{kb+1} in sk[S ^ 1]; K_{kb+2} and V_{kb+1} are loaded meanwhile.
-    // The step is straight-line apart from the rare rescale and mask branches:
-    // on the last tile the scores of the (absent) next tile are still formed,
-    // from stale LDS contents, and never used.
+    // One pipeline step for key tile j (stage S = j % NS): V_j sits in sv[S],
+    // K_{j+1} in sk[(S + 1) % NS].  The two score sets alternate with j % 2.
+    // Waves skip the arithmetic of tiles none of their rows can see but take
+    // part in every load and barrier.  On a wave's last tile the scores of the
+    // next tile are still formed (from whatever the stage holds, always in
+    // bounds) and never used: one branch fewer keeps the step spill-free.
     f32x16 sa[2], sb[2];
     V8 pf[2][2];
-    float mx;
-    auto step = [&](auto st, f32x16 (&sc)[2], f32x16 (&sn)[2], int kb) {
-        constexpr int S = decltype(st)::value;
-        if (kb + 2 < nkb) issue_k(IC<S>{}, kb + 2);
-        if (kb + 1 < nkb) issue_v(IC<S ^ 1>{}, kb + 1);
-        rescale(mx);
-        // phase 1: MFMAs of the next scores beside the softmax of the current ones
-        scores(IC<S ^ 1>{}, sn);
-        softmax(sc, pf);
-        pin(pf);  // P is formed here, not sunk past the mask branch
-        const int kv1 = (kb + 1) * BN;
-        if (kv1 < kend && needs_mask(kv1)) mask(sn, kv1);
-        // phase 2: MFMAs of O += V P beside the row max of the next scores
-        pv(IC<S>{}, pf);
-        rowsum_p(pf);
-        mx = rowmax(sn);
-        wait_vmem();
+    float mx = -INFINITY;
+    auto step = [&](auto st, f32x16 (&sc)[2], f32x16 (&sn)[2], int j) {
+        constexpr int S = decltype(st)::value % NS;
+        if (j + NS - 1 < nkb) issue_v(IC<(S + NS - 1) % NS>{}, j + NS - 1);
+        if (j + NS < nkb) issue_k(IC<S>{}, j + NS);
+        if (j < nkw) {
+            rescale(mx);
+            // phase 1: MFMAs of the next scores beside the softmax of the current ones
+            scores(IC<(S + 1) % NS>{}, sn);
+            softmax(sc, pf);
+            pin(pf);  // P is formed here, not sunk past the mask branch
+            const int kv1 = (j + 1) * BN;
+            if (needs_mask(kv1)) mask(sn, kv1);
+            // phase 2: MFMAs of O += V P beside the row max of the next scores
+            pv(IC<S>{}, pf);
+            rowsum_p(pf);
+            mx = rowmax(sn);
+        }
+        wait_loads<LOADS, 2 * (NS - 2)>(allowance(j));
         __syncthreads();
     };
 
-    // Prologue: K_0, V_0 and K_1 in flight, then S_0 and its row max.
+    // Prologue: K_0, then the requests of steps 1 - NS .. -1 (V_0 .. V_{NS-2},
+    // K_1 .. K_{NS-1}); wait for K_0, V_0 and K_1, form S_0 and its row max.
     issue_k(IC<0>{}, 0);
-    issue_v(IC<0>{}, 0);
-    if (nkb > 1) issue_k(IC<1>{}, 1);
-    wait_vmem();
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((I < nkb ? (issue_v(IC<I>{}, I), 0) : 0, I + 1 < nkb ? (issue_k(IC<I + 1>{}, I + 1), 0) : 0), ...);
+    }(std::make_integer_sequence<int, NS - 1>{});
+    wait_loads<LOADS, 2 * (NS - 2)>(allowance(-1));
     __syncthreads();
-    scores(IC<0>{}, sa);
-    if (needs_mask(0)) mask(sa, 0);
-    mx = rowmax(sa);
-    __syncthreads();  // every wave is done with sk[0] before K_2 refills it
+    if (nkw > 0) {
+        scores(IC<0>{}, sa);
+        if (needs_mask(0)) mask(sa, 0);
+        mx = rowmax(sa);
+    }
+    __syncthreads();  // every wave is done with sk[0] before K_NS refills it
 
-    for (int kb = 0; kb < nkb; kb += 2) {
-        step(IC<0>{}, sa, sb, kb);
-        if (kb + 1 < nkb) step(IC<1>{}, sb, sa, kb + 1);
+    for (int j = 0; j < nkb; j += U) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            ((j + I < nkb ? (I % 2 == 0 ? step(IC<I>{}, sa, sb, j + I) : step(IC<I>{}, sb, sa, j + I)), 0 : 0), ...);
+        }(std::make_integer_sequence<int, U>{});
     }
 
     // Epilogue: O = acc / l, LSE = ln 2 * (m + log2 l).
@@ -400,10 +452,17 @@ void fwd_kernel(FwdParams p)
     }
 }
 
-template <int D, typename T, bool CAUSAL, bool OUT_F32>
-hipError_t launch(const FwdArgs &a, hipStream_t stream)
+// Launch shapes: 8 waves (256 rows per workgroup, one workgroup per CU) when
+// the grid gives every CU such a workgroup, else 4 waves (128 rows, two
+// workgroups per CU); both with a 2-stage ring.  Measured on the 8K d=128
+// causal workload, deeper rings (3 or 4 stages) were no faster: a step's
+// loads already land within the step, and the chip is power-bound there.
+constexpr int kCUs = 256;
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS>
+hipError_t launch_shape(const FwdArgs &a, hipStream_t stream)
 {
-    constexpr int BM = 32 * kNW;
+    constexpr int BM = 32 * NW;
     FwdParams p;
     p.q = a.q;
     p.k = a.k;
@@ -421,8 +480,16 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
     p.c = c < kMinC ? kMinC : c;
     p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_qt));
-    hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, OUT_F32>), grid, dim3(64 * kNW), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, OUT_F32, NW, NS>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32>
+hipError_t launch(const FwdArgs &a, hipStream_t stream)
+{
+    const long long wide_blocks = static_cast<long long>(a.B) * a.H * ((a.Nq + 255) / 256);
+    if (wide_blocks >= kCUs) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2>(a, stream);
+    return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2>(a, stream);
 }
 
 template <int D, typename T>
@@ -441,7 +508,9 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream)
 
 }  // namespace
 
-int fwd_rows_per_block(int) { return 32 * kNW; }
+// The smallest workgroup (rows) any launch shape uses: the grid bound check
+// in the ABI layer is conservative with it.
+int fwd_rows_per_block(int) { return 128; }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 {

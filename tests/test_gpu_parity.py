@@ -69,6 +69,23 @@ def test_ragged_shapes(case):
     assert np.array_equal(lse16, lse)
 
 
+# Grids large enough for the 8-wave launch shape (256 rows per workgroup):
+# ragged query and key counts, waves wholly past Nq, Nq < Nkv.
+WIDE = [
+    # B, H, Nq, Nkv, d, causal, dtype
+    (1, 256, 300, 300, 128, True, "f16"),
+    (2, 128, 257, 500, 64, True, "bf16"),
+    (4, 64, 130, 130, 128, False, "bf16"),
+    (1, 256, 513, 513, 64, True, "f16"),
+    (2, 128, 260, 333, 128, False, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "B{}H{}q{}k{}d{}{}{}".format(c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n", c[6]))
+def test_wide_grid_shapes(case):
+    test_ragged_shapes(case)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.11, 0.7])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_scale_values(scale, dtype):
