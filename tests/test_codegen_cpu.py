@@ -3,6 +3,10 @@
 The half-wave exchange in the prefill kernel relies on both results of the
 permlane32 swap; an earlier form of the helper (a bit cast applied directly to
 a vector element) was lowered by clang as two reads of the first result.
+
+The prefill ring relies on the kernel being spill-free: a scratch reload makes
+the compiler wait for all outstanding vector-memory operations (vmcnt(0)),
+which includes every in-flight K/V tile load.
 """
 import os
 import re
@@ -21,7 +25,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipc
 
 def device_ir(src, tmp_path):
     out = tmp_path / "k.ll"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-I", os.path.join(ROOT, "include"),
                     "-I", CSRC, "-x", "hip", "-S", "--cuda-device-only", "-emit-llvm",
                     os.path.join(CSRC, src), "-o", str(out)], check=True, capture_output=True)
     return out.read_text()
@@ -40,10 +44,35 @@ def test_no_packed_fp32_arithmetic(tmp_path):
     # packed fp32 add/mul/fma are kept out of the kernels
     asm = tmp_path / "k.s"
     for src in ("fa_fwd.hip", "fa_decode.hip"):
-        subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-I", os.path.join(ROOT, "include"),
                         "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip",
                         "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", str(asm)],
                        check=True, capture_output=True)
         text = asm.read_text()
         for op in ("v_pk_add_f32", "v_pk_mul_f32", "v_pk_fma_f32"):
             assert op not in text, f"{op} in {src}"
+
+
+def kernel_metadata(src, tmp_path):
+    asm = tmp_path / (src + ".s")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-I", os.path.join(ROOT, "include"),
+                    "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip",
+                    "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", str(asm)],
+                   check=True, capture_output=True)
+    text = asm.read_text().split("amdhsa.kernels:", 1)[1]
+    kernels = []
+    for block in re.split(r"\n\s+- \.", text)[1:]:
+        fields = dict(re.findall(r"\.(\w+):\s+(\S+)", "." + block))
+        if "name" in fields and "vgpr_spill_count" in fields:  # kernel entries, not argument entries
+            kernels.append(fields)
+    return kernels
+
+
+@pytest.mark.parametrize("src", ["fa_fwd.hip", "fa_decode.hip"])
+def test_kernels_do_not_spill(src, tmp_path):
+    kernels = kernel_metadata(src, tmp_path)
+    assert kernels, f"no kernels found in {src}"
+    for k in kernels:
+        assert int(k["vgpr_spill_count"]) == 0, f"{k['name']} spills {k['vgpr_spill_count']} VGPRs"
+        assert int(k["private_segment_fixed_size"]) == 0, f"{k['name']} uses scratch"
+        assert int(k["vgpr_count"]) <= 256, f"{k['name']}: {k['vgpr_count']} VGPRs leave one wave per SIMD"
