@@ -11,6 +11,11 @@ computes, with citations, is stated at the top of that file:
     S = scale * Q K^T (masked entries -inf), P = softmax(S) row-wise,
     O = P V, LSE = m + ln(l)
 
+and, for the backward with dL/dO = dO, the chain rule through that definition:
+
+    dV = P^T dO, dP = dO V^T, D = rowsum(P * dP), dS = P * (dP - D),
+    dQ = scale * dS K, dK = scale * dS^T Q
+
 All functions pinned by tests/test_oracle_pins.py (brute force at 50 digits,
 torch float64 SDPA, closed forms and invariants); no function here is
 "parity unpinned".
@@ -62,6 +67,9 @@ class Oracle:
                                                  ctypes.c_double, ctypes.POINTER(_i64), _i64,
                                                  _dp, _dp]
         lib.fa_oracle_attention_rows.restype = ctypes.c_int
+        lib.fa_oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64,
+                                                _i64, _i64, ctypes.c_int, ctypes.c_double]
+        lib.fa_oracle_attention_bwd.restype = ctypes.c_int
         lib.fa_oracle_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -121,6 +129,27 @@ class Oracle:
             raise ValueError(f"oracle rejected the call (rc={rc})")
         return o, lse
 
+    def attention_bwd(self, q, k, v, dout, *, causal: bool, scale: float, dtype=None):
+        """(dQ, dK, dV) in float64 for dL/dO = dout; shapes as for attention()."""
+        q, k, v, dout = (self._as_f64(t, dtype) for t in (q, k, v, dout))
+        squeeze = q.ndim == 2
+        if squeeze:
+            q, k, v, dout = q[None, None], k[None, None], v[None, None], dout[None, None]
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d) or dout.shape != q.shape:
+            raise ValueError("shape mismatch")
+        dq = np.empty_like(q)
+        dk = np.empty_like(k)
+        dv = np.empty_like(v)
+        rc = self.lib.fa_oracle_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                              _ptr(dv), B, H, Nq, Nkv, d, int(bool(causal)), float(scale))
+        if rc:
+            raise ValueError(f"oracle rejected the call (rc={rc})")
+        if squeeze:
+            return dq[0, 0], dk[0, 0], dv[0, 0]
+        return dq, dk, dv
+
     def threads(self) -> int:
         return int(self.lib.fa_oracle_threads())
 
@@ -145,6 +174,10 @@ def attention(q, k, v, *, causal, scale, dtype=None):
 
 def attention_rows(q, k, v, rows, *, causal, scale, dtype=None):
     return default().attention_rows(q, k, v, rows, causal=causal, scale=scale, dtype=dtype)
+
+
+def attention_bwd(q, k, v, dout, *, causal, scale, dtype=None):
+    return default().attention_bwd(q, k, v, dout, causal=causal, scale=scale, dtype=dtype)
 
 
 def threads() -> int:

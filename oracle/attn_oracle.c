@@ -230,3 +230,91 @@ int fa_oracle_attention_rows(const double *q, const double *k, const double *v, 
     }
     return failed ? -2 : 0;
 }
+
+/*
+ * Backward of the same attention for a loss L with dL/dO = dO ("FlashAttention
+ * 1-2-3", section "FlashAttention-1: Tiling, Recomputation, and Online Softmax":
+ * the backward keeps per-row statistics instead of the softmax matrix;
+ * "Flash Attention -- Module 12.3", section "Training": the backward is IO-aware
+ * too).  The pages give no formulas; these are the chain rule through the
+ * definition above, written out per head with P materialised:
+ *
+ *   dV[j][c] = sum_i P[i][j] * dO[i][c]
+ *   dP[i][j] = sum_c dO[i][c] * v[j][c]
+ *   D_i      = sum_j P[i][j] * dP[i][j]       (softmax Jacobian: row-wise)
+ *   dS[i][j] = P[i][j] * (dP[i][j] - D_i)
+ *   dQ[i][c] = scale * sum_j dS[i][j] * k[j][c]
+ *   dK[j][c] = scale * sum_i dS[i][j] * q[i][c]
+ *
+ * Invisible keys have P = 0 and so dS = 0.  P is recomputed from q and k here
+ * (the oracle stores nothing between calls).
+ */
+static int head_attention_bwd(const double *q, const double *k, const double *v, const double *dO,
+                              double *dq, double *dk, double *dv, int64_t Nq, int64_t Nkv,
+                              int64_t d, int causal, double scale)
+{
+    double *P = (double *)malloc((size_t)Nq * (size_t)Nkv * sizeof(double));
+    double *dS = (double *)malloc((size_t)Nq * (size_t)Nkv * sizeof(double));
+    if (!P || !dS) {
+        free(P);
+        free(dS);
+        return -2;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < Nq; ++i) {
+        double *p_row = P + i * Nkv, *ds_row = dS + i * Nkv;
+        score_row(q + i * d, k, i, Nq, Nkv, d, causal, scale, p_row);
+        softmax_row(p_row, Nkv);
+        double Di = 0.0;
+        for (int64_t j = 0; j < Nkv; ++j) {
+            double dp = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                dp += dO[i * d + c] * v[j * d + c];
+            ds_row[j] = dp;
+            Di += p_row[j] * dp;
+        }
+        for (int64_t j = 0; j < Nkv; ++j)
+            ds_row[j] = p_row[j] * (ds_row[j] - Di);
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < Nkv; ++j)
+                acc += ds_row[j] * k[j * d + c];
+            dq[i * d + c] = scale * acc;
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < Nkv; ++j) {
+        for (int64_t c = 0; c < d; ++c) {
+            double acc_v = 0.0, acc_k = 0.0;
+            for (int64_t i = 0; i < Nq; ++i) {
+                acc_v += P[i * Nkv + j] * dO[i * d + c];
+                acc_k += dS[i * Nkv + j] * q[i * d + c];
+            }
+            dv[j * d + c] = acc_v;
+            dk[j * d + c] = scale * acc_k;
+        }
+    }
+    free(P);
+    free(dS);
+    return 0;
+}
+
+/*
+ * Gradients over [B][H][N][d] inputs: dO like o, dq like q, dk and dv like k.
+ * Returns 0, -1 for an invalid shape, -2 if a score matrix cannot be allocated.
+ */
+int fa_oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dO,
+                            double *dq, double *dk, double *dv, int64_t B, int64_t H, int64_t Nq,
+                            int64_t Nkv, int64_t d, int causal, double scale)
+{
+    if (B < 0 || H < 0 || check_shape(Nq, Nkv, d, causal))
+        return -1;
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int rc = head_attention_bwd(q + bh * Nq * d, k + bh * Nkv * d, v + bh * Nkv * d,
+                                    dO + bh * Nq * d, dq + bh * Nq * d, dk + bh * Nkv * d,
+                                    dv + bh * Nkv * d, Nq, Nkv, d, causal, scale);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}

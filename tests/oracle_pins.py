@@ -18,7 +18,13 @@ What the pins rest on:
     Online Softmax Trick"): attention over all keys equals the merge of
     attention over two disjoint key sets, for any split point;
   * exact decoding of the 16-bit storage formats, against numpy (binary16)
-    and torch (bfloat16).
+    and torch (bfloat16);
+  * for the backward (dQ, dK, dV given dL/dO): torch float64 autograd through
+    an independently written masked softmax attention, central finite
+    differences of the (separately pinned) forward, and exact invariants:
+    the key-sum of dK vanishes (each softmax row sums to one), the key-sum of
+    dV equals the query-sum of dO, a constant V gives dQ = dK = 0, and the
+    gradients are linear in dO.
 """
 from __future__ import annotations
 
@@ -340,9 +346,93 @@ def pin_widened_inputs(orc):
         assert np.array_equal(o_b, o_v) and np.array_equal(l_b, l_v), f"{dtype} inputs"
 
 
+# ---------------------------------------------------------------------------
+# backward
+
+def _torch_attention_grads(q, k, v, do, causal, scale):
+    """dQ, dK, dV of sum(O * do) by torch float64 autograd on the CPU."""
+    import torch
+    tq, tk, tv = (torch.from_numpy(np.array(x)).requires_grad_(True) for x in (q, k, v))
+    Nq, Nkv = q.shape[-2], k.shape[-2]
+    mask = torch.ones(Nq, Nkv, dtype=torch.bool)
+    if causal:
+        mask = mask.tril(diagonal=Nkv - Nq)
+    s = (tq @ tk.transpose(-1, -2)) * scale
+    p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)
+    o = p @ tv
+    (o * torch.from_numpy(np.array(do))).sum().backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def pin_bwd_torch_autograd(orc):
+    rng = _rng(21)
+    for B, H, Nq, Nkv, d, causal, scale in [(2, 2, 9, 9, 4, True, 0.5), (1, 2, 13, 30, 8, True, 0.35),
+                                            (2, 1, 20, 11, 16, False, 0.25), (1, 1, 7, 7, 3, False, -0.8)]:
+        q = rng.standard_normal((B, H, Nq, d))
+        k = rng.standard_normal((B, H, Nkv, d))
+        v = rng.standard_normal((B, H, Nkv, d))
+        do = rng.standard_normal((B, H, Nq, d))
+        got = orc.attention_bwd(q, k, v, do, causal=causal, scale=scale)
+        ref = _torch_attention_grads(q, k, v, do, causal, scale)
+        for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+            _close(a, b, tol=1e-11, what=f"{name} vs torch autograd {B}x{H}x{Nq}x{Nkv}x{d} causal={causal}")
+
+
+def pin_bwd_finite_difference(orc):
+    # central differences of L = sum(O * dO) through the forward reference
+    rng = _rng(22)
+    Nq, Nkv, d, scale = 6, 9, 5, 0.6
+    for causal in (False, True):
+        q = rng.standard_normal((Nq, d))
+        k = rng.standard_normal((Nkv, d))
+        v = rng.standard_normal((Nkv, d))
+        do = rng.standard_normal((Nq, d))
+        grads = orc.attention_bwd(q, k, v, do, causal=causal, scale=scale)
+        h = 1e-5
+        for which, x in enumerate((q, k, v)):
+            for _ in range(6):
+                idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                lp = float(np.sum(orc.attention(*args_p, causal=causal, scale=scale)[0] * do))
+                lm = float(np.sum(orc.attention(*args_m, causal=causal, scale=scale)[0] * do))
+                fd = (lp - lm) / (2 * h)
+                g = float(grads[which][idx])
+                assert abs(fd - g) <= 1e-7 * max(1.0, abs(g)), \
+                    f"d{'QKV'[which]}{idx} = {g:.12f}, finite difference {fd:.12f} (causal={causal})"
+
+
+def pin_bwd_invariants(orc):
+    rng = _rng(23)
+    B, H, Nq, Nkv, d = 2, 2, 11, 17, 6
+    q = rng.standard_normal((B, H, Nq, d))
+    k = rng.standard_normal((B, H, Nkv, d))
+    v = rng.standard_normal((B, H, Nkv, d))
+    do = rng.standard_normal((B, H, Nq, d))
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_bwd(q, k, v, do, causal=causal, scale=0.4)
+        # each softmax row sums to one, so its dS row sums to zero
+        _close(dk.sum(axis=2), np.zeros((B, H, d)), tol=1e-12, what="key-sum of dK")
+        _close(dv.sum(axis=2), do.sum(axis=2), tol=1e-12, what="key-sum of dV vs query-sum of dO")
+        # constant V: O does not depend on Q or K
+        vc = np.broadcast_to(rng.standard_normal((B, H, 1, d)), v.shape).copy()
+        dq0, dk0, _ = orc.attention_bwd(q, k, vc, do, causal=causal, scale=0.4)
+        _close(dq0, np.zeros_like(dq0), tol=1e-12, what="dQ with constant V")
+        _close(dk0, np.zeros_like(dk0), tol=1e-12, what="dK with constant V")
+        # linear in dO: doubling it doubles every gradient exactly
+        dq2, dk2, dv2 = orc.attention_bwd(q, k, v, 2.0 * do, causal=causal, scale=0.4)
+        assert np.array_equal(dq2, 2.0 * dq) and np.array_equal(dk2, 2.0 * dk) and \
+            np.array_equal(dv2, 2.0 * dv), "gradients not linear in dO"
+
+
 PINS = [
     pin_widen_f16, pin_widen_bf16, pin_decimal_bruteforce, pin_torch_sdpa, pin_two_key_worked,
     pin_constant_v, pin_q_zero, pin_causal_row0, pin_dominant_score, pin_single_key, pin_bounds,
     pin_linearity, pin_permutation, pin_shift_invariance, pin_merge_identity, pin_rows_match_full,
-    pin_head_independence, pin_widened_inputs,
+    pin_head_independence, pin_widened_inputs, pin_bwd_torch_autograd, pin_bwd_finite_difference,
+    pin_bwd_invariants,
 ]

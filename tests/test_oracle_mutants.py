@@ -29,6 +29,17 @@ MUTANTS = [
     ("bf16 exponent bias off by one", "expo - 134", "expo - 133"),
     ("f16 subnormal scale wrong", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     ("max over visible keys skipped", "if (s_row[j] > m)", "if (j == 0 && s_row[j] > m)"),
+    ("backward drops the row term D", "ds_row[j] = p_row[j] * (ds_row[j] - Di);",
+     "ds_row[j] = p_row[j] * ds_row[j];"),
+    ("backward dS sign flipped", "ds_row[j] = p_row[j] * (ds_row[j] - Di);",
+     "ds_row[j] = p_row[j] * (Di - ds_row[j]);"),
+    ("backward dQ misses the scale", "dq[i * d + c] = scale * acc;", "dq[i * d + c] = acc;"),
+    ("backward dP against K instead of V", "dp += dO[i * d + c] * v[j * d + c];",
+     "dp += dO[i * d + c] * k[j * d + c];"),
+    ("backward dV from dS instead of P", "acc_v += P[i * Nkv + j] * dO[i * d + c];",
+     "acc_v += dS[i * Nkv + j] * dO[i * d + c];"),
+    ("backward dK against dO instead of Q", "acc_k += dS[i * Nkv + j] * q[i * d + c];",
+     "acc_k += dS[i * Nkv + j] * dO[i * d + c];"),
 ]
 
 
