@@ -70,6 +70,10 @@ class Oracle:
         lib.fa_oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64,
                                                 _i64, _i64, ctypes.c_int, ctypes.c_double]
         lib.fa_oracle_attention_bwd.restype = ctypes.c_int
+        lib.fa_oracle_attention_bwd_sampled.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int,
+                                                        ctypes.c_double, ctypes.POINTER(_i64), _i64,
+                                                        ctypes.POINTER(_i64), _i64, _dp, _dp, _dp]
+        lib.fa_oracle_attention_bwd_sampled.restype = ctypes.c_int
         lib.fa_oracle_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -150,6 +154,24 @@ class Oracle:
             return dq[0, 0], dk[0, 0], dv[0, 0]
         return dq, dk, dv
 
+    def attention_bwd_sampled(self, q, k, v, dout, qrows, kcols, *, causal: bool, scale: float, dtype=None):
+        """One head: dQ at query rows qrows [n,d], dK and dV at key rows kcols [m,d]."""
+        q, k, v, dout = (self._as_f64(t, dtype) for t in (q, k, v, dout))
+        qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+        kcols = np.ascontiguousarray(kcols, dtype=np.int64)
+        Nq, d = q.shape
+        Nkv = k.shape[0]
+        dq = np.empty((qrows.size, d))
+        dk = np.empty((kcols.size, d))
+        dv = np.empty((kcols.size, d))
+        rc = self.lib.fa_oracle_attention_bwd_sampled(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), Nq, Nkv, d,
+                                                      int(bool(causal)), float(scale), _ptr(qrows, _i64),
+                                                      qrows.size, _ptr(kcols, _i64), kcols.size, _ptr(dq),
+                                                      _ptr(dk), _ptr(dv))
+        if rc:
+            raise ValueError(f"oracle rejected the call (rc={rc})")
+        return dq, dk, dv
+
     def threads(self) -> int:
         return int(self.lib.fa_oracle_threads())
 
@@ -178,6 +200,10 @@ def attention_rows(q, k, v, rows, *, causal, scale, dtype=None):
 
 def attention_bwd(q, k, v, dout, *, causal, scale, dtype=None):
     return default().attention_bwd(q, k, v, dout, causal=causal, scale=scale, dtype=dtype)
+
+
+def attention_bwd_sampled(q, k, v, dout, qrows, kcols, *, causal, scale, dtype=None):
+    return default().attention_bwd_sampled(q, k, v, dout, qrows, kcols, causal=causal, scale=scale, dtype=dtype)
 
 
 def threads() -> int:

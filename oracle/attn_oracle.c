@@ -318,3 +318,110 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v, c
     }
     return 0;
 }
+
+/*
+ * Selected gradients of one head, for spot checks where the whole P does not
+ * fit: the same formulas as head_attention_bwd, evaluated row by row.  A first
+ * pass over every query row i forms LSE_i and D_i (both need the full row of
+ * S and dP); dq rows and dk/dv columns are then sums over one row or one
+ * column of P and dS, each entry recomputed from LSE_i and D_i as
+ * P_ij = exp(S_ij - LSE_i), dS_ij = P_ij * (dP_ij - D_i).
+ * q, dO: [Nq][d]; k, v: [Nkv][d]; qrows / kcols list indices; dq gets
+ * [nq][d], dk and dv [nk][d].  Returns 0, -1 for bad arguments, -2 if out of
+ * memory.
+ */
+int fa_oracle_attention_bwd_sampled(const double *q, const double *k, const double *v, const double *dO,
+                                    int64_t Nq, int64_t Nkv, int64_t d, int causal, double scale,
+                                    const int64_t *qrows, int64_t nq, const int64_t *kcols, int64_t nk,
+                                    double *dq, double *dk, double *dv)
+{
+    if (check_shape(Nq, Nkv, d, causal))
+        return -1;
+    for (int64_t r = 0; r < nq; ++r)
+        if (qrows[r] < 0 || qrows[r] >= Nq)
+            return -1;
+    for (int64_t r = 0; r < nk; ++r)
+        if (kcols[r] < 0 || kcols[r] >= Nkv)
+            return -1;
+    double *lse = (double *)malloc((size_t)(Nq > 0 ? Nq : 1) * sizeof(double));
+    double *Dv = (double *)malloc((size_t)(Nq > 0 ? Nq : 1) * sizeof(double));
+    if (!lse || !Dv) {
+        free(lse);
+        free(Dv);
+        return -2;
+    }
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < Nq; ++i) {
+        double *row = (double *)malloc((size_t)Nkv * 2 * sizeof(double));
+        if (!row) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        double *p_row = row, *dp_row = row + Nkv;
+        score_row(q + i * d, k, i, Nq, Nkv, d, causal, scale, p_row);
+        lse[i] = softmax_row(p_row, Nkv);
+        double Di = 0.0;
+        for (int64_t j = 0; j < Nkv; ++j) {
+            double dp = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                dp += v[j * d + c] * dO[i * d + c];
+            dp_row[j] = dp;
+            Di += p_row[j] * dp;
+        }
+        Dv[i] = Di;
+        free(row);
+    }
+    if (failed) {
+        free(lse);
+        free(Dv);
+        return -2;
+    }
+    /* one entry of P and dS from the row statistics */
+#define P_AT(i, j, pij, dsij)                                                      \
+    do {                                                                           \
+        double s_ = 0.0, dp_ = 0.0;                                                \
+        for (int64_t c_ = 0; c_ < d; ++c_) {                                       \
+            s_ += q[(i) * d + c_] * k[(j) * d + c_];                               \
+            dp_ += dO[(i) * d + c_] * v[(j) * d + c_];                             \
+        }                                                                          \
+        pij = is_visible((i), (j), Nq, Nkv, causal) ? exp(scale * s_ - lse[i]) : 0.0; \
+        dsij = pij * (dp_ - Dv[i]);                                                \
+    } while (0)
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nq; ++r) {
+        int64_t i = qrows[r];
+        for (int64_t c = 0; c < d; ++c)
+            dq[r * d + c] = 0.0;
+        for (int64_t j = 0; j < Nkv; ++j) {
+            double pij, dsij;
+            P_AT(i, j, pij, dsij);
+            (void)pij;
+            for (int64_t c = 0; c < d; ++c)
+                dq[r * d + c] += dsij * k[j * d + c];
+        }
+        for (int64_t c = 0; c < d; ++c)
+            dq[r * d + c] *= scale;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nk; ++r) {
+        int64_t j = kcols[r];
+        for (int64_t c = 0; c < d; ++c)
+            dk[r * d + c] = dv[r * d + c] = 0.0;
+        for (int64_t i = 0; i < Nq; ++i) {
+            double pij, dsij;
+            P_AT(i, j, pij, dsij);
+            for (int64_t c = 0; c < d; ++c) {
+                dv[r * d + c] += pij * dO[i * d + c];
+                dk[r * d + c] += dsij * q[i * d + c];
+            }
+        }
+        for (int64_t c = 0; c < d; ++c)
+            dk[r * d + c] *= scale;
+    }
+#undef P_AT
+    free(lse);
+    free(Dv);
+    return 0;
+}

@@ -429,10 +429,25 @@ def pin_bwd_invariants(orc):
             np.array_equal(dv2, 2.0 * dv), "gradients not linear in dO"
 
 
+def pin_bwd_sampled_matches_full(orc):
+    # the row/column sampling entry against the whole-head backward
+    rng = _rng(24)
+    for Nq, Nkv, d, causal in [(13, 29, 8, True), (20, 20, 16, True), (9, 5, 4, False)]:
+        q, do = rng.standard_normal((Nq, d)), rng.standard_normal((Nq, d))
+        k, v = rng.standard_normal((Nkv, d)), rng.standard_normal((Nkv, d))
+        dq, dk, dv = orc.attention_bwd(q, k, v, do, causal=causal, scale=0.3)
+        qr = np.array([0, Nq - 1, Nq // 2], dtype=np.int64)
+        kc = np.array([Nkv - 1, 0, Nkv // 3], dtype=np.int64)
+        sq, sk, sv = orc.attention_bwd_sampled(q, k, v, do, qr, kc, causal=causal, scale=0.3)
+        _close(sq, dq[qr], tol=1e-12, what="sampled dQ rows")
+        _close(sk, dk[kc], tol=1e-12, what="sampled dK rows")
+        _close(sv, dv[kc], tol=1e-12, what="sampled dV rows")
+
+
 PINS = [
     pin_widen_f16, pin_widen_bf16, pin_decimal_bruteforce, pin_torch_sdpa, pin_two_key_worked,
     pin_constant_v, pin_q_zero, pin_causal_row0, pin_dominant_score, pin_single_key, pin_bounds,
     pin_linearity, pin_permutation, pin_shift_invariance, pin_merge_identity, pin_rows_match_full,
     pin_head_independence, pin_widened_inputs, pin_bwd_torch_autograd, pin_bwd_finite_difference,
-    pin_bwd_invariants,
+    pin_bwd_invariants, pin_bwd_sampled_matches_full,
 ]

@@ -40,6 +40,8 @@ MUTANTS = [
      "acc_v += dS[i * Nkv + j] * dO[i * d + c];"),
     ("backward dK against dO instead of Q", "acc_k += dS[i * Nkv + j] * q[i * d + c];",
      "acc_k += dS[i * Nkv + j] * dO[i * d + c];"),
+    ("sampled backward drops D", "dsij = pij * (dp_ - Dv[i]);", "dsij = pij * dp_;"),
+    ("sampled backward row term from the wrong row", "Dv[i] = Di;", "Dv[i] = Di * 0.5;"),
 ]
 
 
