@@ -14,7 +14,10 @@ from ._binding import (  # noqa: F401
     FA_OUT_F32,
     LIBRARY,
     FaError,
+    bwd,
     decode,
+    fa_bwd,
+    fa_bwd_workspace_size,
     fa_decode,
     fa_decode_num_splits,
     fa_decode_workspace_size,

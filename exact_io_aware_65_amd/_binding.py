@@ -5,9 +5,10 @@ kernels of libfa355.so.  PyTorch supplies device memory and the current
 stream.  The library must have been built (``python -m
 exact_io_aware_65_amd.build``); there is no fallback of any kind.
 
-Thin wrappers with the C names (``fa_fwd``, ``fa_decode``, ...) take device
-pointers or tensors and raise :class:`FaError` on a non-OK status.  The
-convenience functions :func:`fwd` and :func:`decode` allocate the outputs.
+Thin wrappers with the C names (``fa_fwd``, ``fa_decode``, ``fa_bwd``, ...)
+take device pointers or tensors and raise :class:`FaError` on a non-OK
+status.  The convenience functions :func:`fwd`, :func:`decode` and
+:func:`bwd` allocate the outputs.
 """
 from __future__ import annotations
 
@@ -48,6 +49,10 @@ def library() -> ctypes.CDLL:
         lib.fa_decode_workspace_size.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i, i, i, i]
         lib.fa_decode_num_splits.restype = i
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
+        lib.fa_bwd.restype = i
+        lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+        lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
         lib.fa_status_str.argtypes = [i]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_last_error.restype = ctypes.c_char_p
@@ -91,6 +96,17 @@ def fa_decode_workspace_size(B, H, Nkv, d, num_splits=0) -> int:
 
 def fa_decode_num_splits(B, H, Nkv, d) -> int:
     return int(library().fa_decode_num_splits(B, H, Nkv, d))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, causal, scale, dtype, workspace,
+           workspace_bytes, stream=None) -> None:
+    _check(library().fa_bwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(dout), _addr(lse), _addr(dq),
+                            _addr(dk), _addr(dv), B, H, Nq, Nkv, d, int(bool(causal)), float(scale), int(dtype),
+                            _addr(workspace), int(workspace_bytes), _addr(stream)))
+
+
+def fa_bwd_workspace_size(B, H, Nq) -> int:
+    return int(library().fa_bwd_workspace_size(B, H, Nq))
 
 
 def fa_status_str(status: int) -> str:
@@ -182,3 +198,36 @@ def decode(q, k, v, *, scale=None, num_splits=0, out_dtype=None):
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, code, num_splits, ws, nbytes, _stream(q.device))
     return o, lse
+
+
+def bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, out_dtype=None):
+    """Gradients (dq, dk, dv) of fwd for dL/do = dout, from fwd's o (q's dtype) and lse.
+
+    out_dtype may be torch.float32 to get the gradients in fp32, else they
+    have q's dtype."""
+    import torch
+    _check_inputs(q, k, v)
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    code = _dtype_code(q)
+    gdt = q.dtype
+    if out_dtype is not None and out_dtype != q.dtype:
+        if out_dtype != torch.float32:
+            raise TypeError("out_dtype must be None, q.dtype or torch.float32")
+        code |= FA_OUT_F32
+        gdt = torch.float32
+    dq = torch.empty(q.shape, dtype=gdt, device=q.device)
+    dk = torch.empty(k.shape, dtype=gdt, device=q.device)
+    dv = torch.empty(v.shape, dtype=gdt, device=q.device)
+    nbytes = fa_bwd_workspace_size(B, H, Nq)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, causal, scale, code, ws, nbytes, _stream(q.device))
+    return dq, dk, dv

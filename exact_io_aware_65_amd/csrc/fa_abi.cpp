@@ -4,6 +4,7 @@
 // the device nor the outputs.
 #include "fa355.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -212,6 +213,84 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
         std::fprintf(stderr, "fa355: fa_decode B=%d H=%d Nkv=%d d=%d dtype=0x%x splits=%d chunk=%d\n", B, H,
                      Nkv, d, dtype, splits, chunk);
     const hipError_t err = fa355::launch_decode(a, stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return FA_OK;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int Nq)
+{
+    if (B < 0 || H < 0 || Nq < 0) return 0;
+    return fa355::bwd_workspace_bytes(B, H, Nq);
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+           void *dq, void *dk, void *dv, int B, int H, int Nq, int Nkv, int d, int causal, float scale,
+           int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    static const char *fn = "fa_bwd";
+    fa355::Elem elem;
+    bool out_f32;
+    int rc = parse_dtype(fn, dtype, &elem, &out_f32);
+    if (rc) return rc;
+    if ((rc = check_head_dim(fn, d))) return rc;
+    if (B < 0 || H < 0 || Nq < 0 || Nkv < 0)
+        return fail(FA_ERR_INVALID, "%s: negative size (B=%d H=%d Nq=%d Nkv=%d)", fn, B, H, Nq, Nkv);
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "%s: scale must be finite", fn);
+    if (B == 0 || H == 0) return FA_OK;
+    if (Nkv == 0) return fail(FA_ERR_INVALID, "%s: Nkv=0: attention over no keys is undefined", fn);
+    if (causal && Nq > Nkv)
+        return fail(FA_ERR_INVALID, "%s: causal attention needs Nq <= Nkv (got %d > %d)", fn, Nq, Nkv);
+    const void *in16[5] = {q, k, v, o, dout};
+    void *outs[3] = {dq, dk, dv};
+    for (const void *ptr : in16)
+        if (!ptr || misaligned(ptr, 16))
+            return fail(FA_ERR_INVALID, "%s: q, k, v, o and dout must be non-NULL and 16-byte aligned", fn);
+    for (const void *ptr : outs)
+        if (!ptr || misaligned(ptr, 16))
+            return fail(FA_ERR_INVALID, "%s: dq, dk and dv must be non-NULL and 16-byte aligned", fn);
+    if (!lse || misaligned(lse, 4)) return fail(FA_ERR_INVALID, "%s: lse must be non-NULL and 4-byte aligned", fn);
+    const unsigned __int128 bh = static_cast<unsigned __int128>(B) * H;
+    const unsigned __int128 nq_el = bh * Nq * d, nkv_el = bh * Nkv * d;
+    if (nq_el >= kMaxElems || nkv_el >= kMaxElems)
+        return fail(FA_ERR_INVALID, "%s: tensor sizes exceed 2^62 elements", fn);
+    const int oel = out_f32 ? 4 : 2;
+    if (static_cast<unsigned long long>(Nkv) * d * oel > 0xffffffffULL ||
+        static_cast<unsigned long long>(Nq) * d * oel > 0xffffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: one head of a tensor exceeds 4 GiB", fn);
+    const long long blocks = static_cast<long long>(B) * H * ((std::max(Nq, Nkv) + 127) / 128);
+    if (blocks > 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+    const size_t need = fa355::bwd_workspace_bytes(B, H, Nq);
+    if (need && (!workspace || misaligned(workspace, 16) || workspace_bytes < need))
+        return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)", fn,
+                    need, workspace_bytes, workspace);
+    const Span ins[6] = {span("q", q, nq_el * 2),    span("k", k, nkv_el * 2),      span("v", v, nkv_el * 2),
+                         span("o", o, nq_el * 2),    span("dout", dout, nq_el * 2), span("lse", lse, bh * Nq * 4)};
+    const Span outspans[3] = {span("dq", dq, nq_el * oel), span("dk", dk, nkv_el * oel), span("dv", dv, nkv_el * oel)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Span &s : ins)
+            if (outspans[i].hi > outspans[i].lo && s.hi > s.lo && overlap(outspans[i], s))
+                return fail(FA_ERR_INVALID, "%s: %s overlaps %s", fn, outspans[i].name, s.name);
+        for (int j = i + 1; j < 3; ++j)
+            if (outspans[i].hi > outspans[i].lo && outspans[j].hi > outspans[j].lo && overlap(outspans[i], outspans[j]))
+                return fail(FA_ERR_INVALID, "%s: %s overlaps %s", fn, outspans[i].name, outspans[j].name);
+    }
+    if (need) {
+        const Span ws = span("workspace", workspace, need);
+        for (const Span &s : ins)
+            if (s.hi > s.lo && overlap(ws, s)) return fail(FA_ERR_WORKSPACE, "%s: workspace overlaps %s", fn, s.name);
+        for (const Span &s : outspans)
+            if (s.hi > s.lo && overlap(ws, s)) return fail(FA_ERR_WORKSPACE, "%s: workspace overlaps %s", fn, s.name);
+    }
+
+    float *ws_l2 = static_cast<float *>(workspace);
+    float *ws_dd = ws_l2 ? ws_l2 + static_cast<size_t>(B) * H * Nq : nullptr;
+    fa355::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, causal != 0, scale, elem, out_f32,
+                     ws_l2, ws_dd};
+    if (log_enabled())
+        std::fprintf(stderr, "fa355: fa_bwd B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x\n", B, H, Nq, Nkv, d,
+                     causal != 0, dtype);
+    const hipError_t err = fa355::launch_bwd(a, stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
     return FA_OK;
 }

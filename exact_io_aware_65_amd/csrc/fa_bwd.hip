@@ -1,0 +1,530 @@
+// Attention backward for gfx950: dQ, dK, dV given dL/dO, from the forward's
+// inputs, its output O and its per-row log-sum-exp.
+//
+// The forward keeps only one statistic per query row (LSE) instead of the
+// softmax matrix, and the backward recomputes P tile by tile from it ("FlashAttention
+// 1-2-3: The IO-Aware Revolution in LLM Inference", section "FlashAttention-1:
+// Tiling, Recomputation, and Online Softmax"); like the forward it never
+// writes an Nq x Nkv matrix to HBM ("Flash Attention -- Module 12.3", section
+// "Training").  With z = scale * q.k, P = exp(z - LSE) and the chain rule:
+//
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO[i][c] O[i][c] (= sum_j P_ij dP_ij),
+//   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Three kernels, all on one stream:
+//   bwd_prep_kernel   per query row: D_i and the base-2 LSE, into the workspace;
+//   bwd_dkdv_kernel   key blocks outer (each wave owns 32 keys, K and V in
+//                     registers), query tiles streamed through LDS; accumulates
+//                     dV^T += dO^T P and dK^T += Q^T dS in registers;
+//   bwd_dq_kernel     query blocks outer (each wave owns 32 queries, Q and dO
+//                     in registers), key tiles streamed through LDS;
+//                     accumulates dQ^T += K^T dS^T.
+// Recomputing S and dP in both of the last two kernels costs 7 products
+// instead of 5, but no partial sums cross workgroups: no atomics, results are
+// deterministic.
+//
+// MFMA layouts (32x32x16, lane l holds column l % 32 of the accumulator):
+//   dK/dV kernel: S = Q K^T with the Q rows fed in swap23 order, so a lane
+//     holds, for its key, the queries {8h..8h+7, 16+8h..16+8h+7}: exactly the
+//     B-operand k-slots of dV^T = dO^T P and dK^T = Q^T dS, so P and dS go to
+//     the second products without lane movement (as P does in the forward).
+//   dQ kernel: S^T = K Q^T, as in the forward; dS^T is the B operand of
+//     dQ^T = K^T dS^T.
+// Tiles read both as rows (b128) and transposed (ds_read_b64_tr_b16) -- Q and
+// dO in the dK/dV kernel, K in the dQ kernel -- use a chunk permutation that
+// is conflict-free for both reads (see dswz).
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+#include <type_traits>
+
+namespace fa355 {
+namespace {
+
+constexpr float kBwdMinC = 1e-30f;  // as the forward: a zero scale keeps -inf * c = -inf
+
+struct BwdParams {
+    const void *q, *k, *v, *dout;
+    void *dq, *dk, *dv;
+    const float *l2;   // [BH][Nq] LSE * log2(e)
+    const float *dd;   // [BH][Nq] D_i = rowsum(dO * O)
+    int Nq, Nkv, n_bh, n_tiles;
+    float c;           // max(|scale| * log2(e), kBwdMinC)
+    float scale;       // signed scale: the dQ and dK factor
+    uint32_t sign;     // 0x80008000 when scale < 0: K (dK/dV kernel) or Q (dQ kernel) is negated on load
+};
+
+struct PrepParams {
+    const void *o, *dout;
+    const float *lse;
+    float *l2, *dd;
+    long long rows;
+};
+
+// The MFMA row that lane l % 32 feeds is row swap23(l % 32) of the tile.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// Chunk permutations (XOR on the 16-byte chunk index of a row).
+// kswz: rows read as 16-byte runs only (16 lanes, rows swap23(0..15)).
+// dswz: rows read both as 16-byte runs and transposed (32 lanes covering 4
+// consecutive rows x 64 bytes).  d = 128: the row's low nibble with its two
+// halves exchanged; d = 64: bit 1 of the row to chunk bit 2, bits 2-3 to
+// chunk bits 0-1 (two rows share a 256-byte bank line).
+template <int D> __device__ __forceinline__ int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D> __device__ __forceinline__ int dswz(int row)
+{
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+// ---------------------------------------------------------------------------
+// Per query row: D = sum_c dO * O (fp32 from the 16-bit values) and LSE in
+// base 2.  D/8 lanes per row, 16 bytes each.
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p)
+{
+    constexpr int LPR = D / 8, RPB = 256 / LPR;
+    const int tid = threadIdx.x, part = tid % LPR;
+    const long long row = static_cast<long long>(blockIdx.x) * RPB + tid / LPR;
+    float acc = 0.f;
+    if (row < p.rows) {
+        const size_t off = static_cast<size_t>(row) * D * 2 + part * 16;
+        const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.o) + off);
+        const u32x4 g = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.dout) + off);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = dot2<T>(o[j], g[j], acc);
+    }
+    acc = group_sum<LPR>(acc);
+    if (part == 0 && row < p.rows) {
+        p.dd[row] = acc;
+        p.l2[row] = p.lse[row] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key blocks of 128 (4 waves x 32 keys), query tiles of 64 (two
+// 32-query sub-tiles) through a two-stage LDS ring.
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
+void bwd_dkdv_kernel(BwdParams p)
+{
+    constexpr int NW = 4, BK = 32 * NW, BQ = 64, NT = 64 * NW;
+    constexpr int DC = D / 8, TILE = BQ * DC, LOADS = TILE / NT, ROWB = 2 * D, KS = D / 16, DT = D / 32;
+    static_assert(TILE % NT == 0, "tile must split evenly over the threads");
+    using V8 = typename Vec<T>::v8;
+
+    __shared__ u32x4 sq[2][TILE];   // Q tiles [query][dim], dswz-permuted
+    __shared__ u32x4 sdo[2][TILE];  // dO tiles [query][dim], dswz-permuted
+    __shared__ float sl2[2][BQ];    // base-2 LSE of the tile's queries
+    __shared__ float sdd[2][BQ];    // D of the tile's queries
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 31, h = lane >> 5;
+
+    // Causal: key blocks near the start see the most queries; they go first.
+    const int bh = blockIdx.x % p.n_bh;
+    const int kt = static_cast<int>(blockIdx.x / p.n_bh);
+    const int k0 = kt * BK;
+    const int kw0 = k0 + 32 * wave;
+    const int key = kw0 + c;
+    const int off = p.Nkv - p.Nq;  // row i sees keys j <= i + off
+    const int nqt = (p.Nq + BQ - 1) / BQ;
+    // first query tile any key of the block can be seen from; a wave's own first query row
+    const int t0 = CAUSAL ? max(0, k0 - off) / BQ : 0;
+    const int wfirst = CAUSAL ? kw0 - off : 0;
+
+    const size_t qh = static_cast<size_t>(bh) * p.Nq * ROWB, kh = static_cast<size_t>(bh) * p.Nkv * ROWB;
+    const u32x4 rq = make_rsrc_words(static_cast<const char *>(p.q) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+    const u32x4 rdo = make_rsrc_words(static_cast<const char *>(p.dout) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+    const u32x4 rl2 = make_rsrc_words(p.l2 + static_cast<size_t>(bh) * p.Nq, static_cast<uint32_t>(p.Nq) * 4);
+    const u32x4 rdd = make_rsrc_words(p.dd + static_cast<size_t>(bh) * p.Nq, static_cast<uint32_t>(p.Nq) * 4);
+
+    // K and V as B operands of S = Q K^T and dP = dO V^T: lane (c, h) holds key
+    // kw0 + c, dims 16 s + 8 h .. + 7 (zeros past Nkv).  K carries the sign of
+    // the scale.
+    V8 kf[KS], vf[KS];
+    {
+        const auto rk = make_rsrc(static_cast<const char *>(p.k) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+        const auto rv = make_rsrc(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kf[s] = as<V8>(buffer_load16(rk, key * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.sign);
+            vf[s] = as<V8>(buffer_load16(rv, key * ROWB + (16 * s + 8 * h) * 2, 0));
+        }
+    }
+
+    auto ld_off = [&](int i) {
+        const int pch = (wave * LOADS + i) * 64 + lane;
+        const int row = pch / DC, col = pch % DC;
+        return static_cast<uint32_t>(row * ROWB + ((col ^ dswz<D>(row)) << 4));
+    };
+    auto issue = [&](int st, int t) {
+        const uint32_t tq = static_cast<uint32_t>(t) * BQ * ROWB;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            dma_to_lds16(rq, ld_off(i), tq, &sq[st][(wave * LOADS + i) * 64]);
+            dma_to_lds16(rdo, ld_off(i), tq, &sdo[st][(wave * LOADS + i) * 64]);
+        }
+        if (wave == 0) {
+            dma_to_lds4(rl2, lane * 4, static_cast<uint32_t>(t) * BQ * 4, &sl2[st][0]);
+            dma_to_lds4(rdd, lane * 4, static_cast<uint32_t>(t) * BQ * 4, &sdd[st][0]);
+        }
+    };
+
+    // Row reads of Q and dO (A operands of S and dP): row swap23(c) (+ 32 per
+    // sub-tile), logical chunk 2 s + h.
+    uint32_t ra0;
+    {
+        const int r = swap23(c);
+        ra0 = r * ROWB + ((h ^ dswz<D>(r)) << 4);
+    }
+    // Transposed reads (A operands of dV^T = dO^T P and dK^T = Q^T dS): lane
+    // 16 g + 4 j + q addresses query 8 (g / 2) + j + 4 half (+ 16 u + 32 per
+    // sub-tile) and dims 32 dt + 16 (g % 2) + 4 q .. + 3.  The permutation
+    // depends on half; dt enters as an XOR on bits 6.. of the offset.
+    uint32_t ta0[2];
+    {
+        const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int r = 8 * (g >> 1) + j + 4 * half;
+            ta0[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
+        }
+    }
+
+    f32x16 dvacc[DT], dkacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dvacc[dt][e] = dkacc[dt][e] = 0.f;
+    const float cs = p.c;
+
+    auto subtile = [&](int st, int t, int qq) {
+        const char *SQ = reinterpret_cast<const char *>(sq[st]);
+        const char *SDO = reinterpret_cast<const char *>(sdo[st]);
+        const int qs0 = t * BQ + 32 * qq;  // first query of the sub-tile
+        // S = Q K^T and dP = dO V^T (rows: queries in swap23 order; columns: keys)
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint32_t a = (ra0 ^ (ks << 5)) + qq * 32 * ROWB;
+            s = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SQ + a)), kf[ks], s);
+            dp = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SDO + a)), vf[ks], dp);
+        }
+        // this lane's queries: element e <-> query 8 h + e (e < 8), 16 + 8 h + e - 8
+        const f32x4 *l2v = reinterpret_cast<const f32x4 *>(&sl2[st][32 * qq + 8 * h]);
+        const f32x4 *ddv = reinterpret_cast<const f32x4 *>(&sdd[st][32 * qq + 8 * h]);
+        const f32x4 l2a[4] = {l2v[0], l2v[1], l2v[4], l2v[5]};
+        const f32x4 dda[4] = {ddv[0], ddv[1], ddv[4], ddv[5]};
+        const bool edge = qs0 + 32 > p.Nq || (CAUSAL && kw0 + 31 > qs0 + off);
+        u32x4 pw[2], dw[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float pr[2], dr[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int e = 8 * u + 2 * j + b;
+                    const float l2 = l2a[e / 4][e % 4], dd = dda[e / 4][e % 4];
+                    float pe = fast_exp2(fmaf(s[e], cs, -l2));
+                    if (edge) {
+                        const int qi = qs0 + 16 * u + 8 * h + 2 * j + b;
+                        if (qi >= p.Nq || (CAUSAL && key > qi + off)) pe = 0.f;
+                    }
+                    pr[b] = pe;
+                    dr[b] = pe * (dp[e] - dd);
+                }
+                pw[u][j] = pack2<T>(pr[0], pr[1]);
+                dw[u][j] = pack2<T>(dr[0], dr[1]);
+            }
+        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint32_t rowoff = (qq * 32 + 16 * u) * ROWB;
+                const uint32_t a0 = (ta0[0] ^ (dt << 6)) + rowoff, a1 = (ta0[1] ^ (dt << 6)) + rowoff;
+                const u32x2 do_lo = lds_read_tr16(SDO + a0), do_hi = lds_read_tr16(SDO + a1);
+                const u32x2 q_lo = lds_read_tr16(SQ + a0), q_hi = lds_read_tr16(SQ + a1);
+                dvacc[dt] = mfma32(as<V8>(u32x4{do_lo[0], do_lo[1], do_hi[0], do_hi[1]}), as<V8>(pw[u]), dvacc[dt]);
+                dkacc[dt] = mfma32(as<V8>(u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}), as<V8>(dw[u]), dkacc[dt]);
+            }
+    };
+
+    if (t0 < nqt) issue(0, t0);
+    for (int t = t0; t < nqt; ++t) {
+        const int st = (t - t0) & 1;
+        wait_vmcnt<0>();
+        __syncthreads();  // tile t visible to every wave; tile t - 1's stage free
+        if (t + 1 < nqt) issue(st ^ 1, t + 1);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            const int qs0 = t * BQ + 32 * qq;
+            // some (query, key) pair of the sub-tile is visible to this wave
+            if (qs0 < p.Nq && (!CAUSAL || qs0 + 31 >= wfirst)) subtile(st, t, qq);
+        }
+    }
+
+    // Epilogue: lane (c, h) writes key kw0 + c, dims 32 dt + 8 j + 4 h .. + 3.
+    if (key < p.Nkv) {
+        const size_t orow = (static_cast<size_t>(bh) * p.Nkv + key) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 32 * dt + 8 * j + 4 * h;
+                const f32x4 v4 = {dvacc[dt][4 * j], dvacc[dt][4 * j + 1], dvacc[dt][4 * j + 2], dvacc[dt][4 * j + 3]};
+                const f32x4 k4 = {dkacc[dt][4 * j] * p.scale, dkacc[dt][4 * j + 1] * p.scale,
+                                  dkacc[dt][4 * j + 2] * p.scale, dkacc[dt][4 * j + 3] * p.scale};
+                if constexpr (OUT_F32) {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dv) + orow + d0) = v4;
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dk) + orow + d0) = k4;
+                } else {
+                    *reinterpret_cast<u32x2 *>(static_cast<T *>(p.dv) + orow + d0) =
+                        u32x2{pack2<T>(v4[0], v4[1]), pack2<T>(v4[2], v4[3])};
+                    *reinterpret_cast<u32x2 *>(static_cast<T *>(p.dk) + orow + d0) =
+                        u32x2{pack2<T>(k4[0], k4[1]), pack2<T>(k4[2], k4[3])};
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query blocks of 128 (4 waves x 32 queries), key tiles of 64 through a
+// two-stage LDS ring, as in the forward.
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p)
+{
+    constexpr int NW = 4, BM = 32 * NW, BN = 64, NT = 64 * NW;
+    constexpr int DC = D / 8, TILE = BN * DC, LOADS = TILE / NT, ROWB = 2 * D, KS = D / 16, DT = D / 32;
+    static_assert(TILE % NT == 0, "tile must split evenly over the threads");
+    using V8 = typename Vec<T>::v8;
+
+    __shared__ u32x4 sk[2][TILE];  // K tiles, dswz (row and transposed reads)
+    __shared__ u32x4 sv[2][TILE];  // V tiles, kswz (row reads)
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 31, h = lane >> 5;
+
+    const int bh = blockIdx.x % p.n_bh;
+    const int qt = p.n_tiles - 1 - static_cast<int>(blockIdx.x / p.n_bh);  // heavy causal tiles first
+    const int q0 = qt * BM;
+    const int wq0 = q0 + 32 * wave;
+    const int qrow = wq0 + c;
+    const int off = p.Nkv - p.Nq;
+    int kend = p.Nkv;
+    if constexpr (CAUSAL) kend = min(p.Nkv, min(q0 + BM, p.Nq) + off);
+    const int nkb = (kend + BN - 1) / BN;
+
+    const size_t qh = static_cast<size_t>(bh) * p.Nq * ROWB, kh = static_cast<size_t>(bh) * p.Nkv * ROWB;
+    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+    const u32x4 rv = make_rsrc_words(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+
+    // Q (sign of the scale folded in) and dO as B operands: lane (c, h) holds
+    // query qrow, dims 16 s + 8 h .. + 7.
+    V8 qf[KS], gf[KS];
+    {
+        const auto rq = make_rsrc(static_cast<const char *>(p.q) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+        const auto rdo = make_rsrc(static_cast<const char *>(p.dout) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qf[s] = as<V8>(buffer_load16(rq, qrow * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.sign);
+            gf[s] = as<V8>(buffer_load16(rdo, qrow * ROWB + (16 * s + 8 * h) * 2, 0));
+        }
+    }
+    const bool live = qrow < p.Nq;
+    const float l2 = live ? p.l2[static_cast<size_t>(bh) * p.Nq + qrow] : 0.f;
+    const float dd = live ? p.dd[static_cast<size_t>(bh) * p.Nq + qrow] : 0.f;
+
+    auto ld_off = [&](int i, bool dual) {
+        const int pch = (wave * LOADS + i) * 64 + lane;
+        const int row = pch / DC, col = pch % DC;
+        return static_cast<uint32_t>(row * ROWB + ((col ^ (dual ? dswz<D>(row) : kswz<D>(row))) << 4));
+    };
+    auto issue = [&](int st, int kb) {
+        const uint32_t tk = static_cast<uint32_t>(kb) * BN * ROWB;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            dma_to_lds16(rk, ld_off(i, true), tk, &sk[st][(wave * LOADS + i) * 64]);
+            dma_to_lds16(rv, ld_off(i, false), tk, &sv[st][(wave * LOADS + i) * 64]);
+        }
+    };
+
+    // Row reads of K (dswz) and V (kswz): row 32 kk + swap23(c), chunk 2 s + h.
+    uint32_t ka0, va0;
+    {
+        const int r = swap23(c);
+        ka0 = r * ROWB + ((h ^ dswz<D>(r)) << 4);
+        va0 = r * ROWB + ((h ^ kswz<D>(r)) << 4);
+    }
+    // Transposed reads of K (A operand of dQ^T = K^T dS^T), as in the dK/dV kernel.
+    uint32_t ta0[2];
+    {
+        const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int r = 8 * (g >> 1) + j + 4 * half;
+            ta0[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
+        }
+    }
+
+    f32x16 dqacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dqacc[dt][e] = 0.f;
+    const float cs = p.c;
+
+    auto tile = [&](int st, int kv0) {
+        const char *SK = reinterpret_cast<const char *>(sk[st]);
+        const char *SV = reinterpret_cast<const char *>(sv[st]);
+        // S^T = K Q^T and dP^T = V dO^T (rows: keys in swap23 order; columns: queries)
+        f32x16 s[2] = {}, dp[2] = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 xk = *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ (ks << 5)) + kk * 32 * ROWB);
+                const u32x4 xv = *reinterpret_cast<const u32x4 *>(SV + (va0 ^ (ks << 5)) + kk * 32 * ROWB);
+                s[kk] = mfma32(as<V8>(xk), qf[ks], s[kk]);
+                dp[kk] = mfma32(as<V8>(xv), gf[ks], dp[kk]);
+            }
+        const bool edge = (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
+        u32x4 dw[2][2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float dr[2];
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        const int e = 8 * u + 2 * j + b;
+                        float pe = fast_exp2(fmaf(s[kk][e], cs, -l2));
+                        if (edge) {
+                            const int kj = kv0 + 32 * kk + 16 * u + 8 * h + 2 * j + b;
+                            if (kj >= p.Nkv || (CAUSAL && kj > qrow + off)) pe = 0.f;
+                        }
+                        dr[b] = pe * (dp[kk][e] - dd);
+                    }
+                    dw[kk][u][j] = pack2<T>(dr[0], dr[1]);
+                }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const uint32_t rowoff = (32 * kk + 16 * u) * ROWB;
+                    const u32x2 lo = lds_read_tr16(SK + ((ta0[0] ^ (dt << 6)) + rowoff));
+                    const u32x2 hi = lds_read_tr16(SK + ((ta0[1] ^ (dt << 6)) + rowoff));
+                    dqacc[dt] = mfma32(as<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), as<V8>(dw[kk][u]), dqacc[dt]);
+                }
+    };
+
+    if (nkb > 0) issue(0, 0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int st = kb & 1;
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (kb + 1 < nkb) issue(st ^ 1, kb + 1);
+        const int kv0 = kb * BN;
+        // wave-uniform: the products mix operands across lanes, so a wave runs
+        // them whole; columns of rows past Nq are formed and never stored
+        if (wq0 < p.Nq && (!CAUSAL || kv0 <= wq0 + 31 + off)) tile(st, kv0);
+    }
+
+    if (live) {
+        const size_t orow = (static_cast<size_t>(bh) * p.Nq + qrow) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 32 * dt + 8 * j + 4 * h;
+                const f32x4 v4 = {dqacc[dt][4 * j] * p.scale, dqacc[dt][4 * j + 1] * p.scale,
+                                  dqacc[dt][4 * j + 2] * p.scale, dqacc[dt][4 * j + 3] * p.scale};
+                if constexpr (OUT_F32)
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dq) + orow + d0) = v4;
+                else
+                    *reinterpret_cast<u32x2 *>(static_cast<T *>(p.dq) + orow + d0) =
+                        u32x2{pack2<T>(v4[0], v4[1]), pack2<T>(v4[2], v4[3])};
+            }
+    }
+}
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32>
+hipError_t launch(const BwdArgs &a, hipStream_t stream)
+{
+    // With Nq = 0 only the key pass runs: it writes dK = dV = 0.
+    const long long rows = static_cast<long long>(a.B) * a.H * a.Nq;
+    hipError_t err;
+    if (rows > 0) {
+        PrepParams pp{a.o, a.dout, a.lse, a.ws_l2, a.ws_dd, rows};
+        constexpr int RPB = 256 / (D / 8);
+        hipLaunchKernelGGL((bwd_prep_kernel<D, T>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)), dim3(256), 0,
+                           stream, pp);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+
+    BwdParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.dout = a.dout;
+    p.dq = a.dq;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.l2 = a.ws_l2;
+    p.dd = a.ws_dd;
+    p.Nq = a.Nq;
+    p.Nkv = a.Nkv;
+    p.n_bh = a.B * a.H;
+    const float c = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
+    p.c = c < kBwdMinC ? kBwdMinC : c;
+    p.scale = a.scale;
+    p.sign = a.scale < 0.f ? 0x80008000u : 0u;
+
+    p.n_tiles = (a.Nkv + 127) / 128;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, OUT_F32>),
+                       dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    p.n_tiles = (a.Nq + 127) / 128;
+    if (p.n_tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, OUT_F32>),
+                       dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, typename T>
+hipError_t launch_dt(const BwdArgs &a, hipStream_t stream)
+{
+    if (a.causal)
+        return a.out_f32 ? launch<D, T, true, true>(a, stream) : launch<D, T, true, false>(a, stream);
+    return a.out_f32 ? launch<D, T, false, true>(a, stream) : launch<D, T, false, false>(a, stream);
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs &a, hipStream_t stream)
+{
+    return a.elem == Elem::F16 ? launch_dt<D, _Float16>(a, stream) : launch_dt<D, __bf16>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream)
+{
+    if (a.d == 64) return launch_d<64>(a, stream);
+    if (a.d == 128) return launch_d<128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa355

@@ -143,7 +143,20 @@ __device__ __forceinline__ void dma_to_lds16(u32x4 rsrc, uint32_t voff, uint32_t
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
                  :
-                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0), "n"(IMM)
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(m0), "n"(IMM)
+                 : "memory");
+}
+
+// As dma_to_lds16 with 4 bytes per lane: lane i's dword lands at
+// lds_base + IMM + 4 * i.
+template <int IMM = 0>
+__device__ __forceinline__ void dma_to_lds4(u32x4 rsrc, uint32_t voff, uint32_t soff, const void *lds_base)
+{
+    static_assert(IMM >= 0 && IMM < 4096, "12-bit instruction offset");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen offset:%4 lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(m0), "n"(IMM)
                  : "memory");
 }
 

@@ -37,11 +37,31 @@ struct DecodeArgs {
     float *ws_lse;   // [B*H][splits] partial log2-sum-exp values
 };
 
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;  // o: the forward output in the input type
+    const float *lse;                   // [B*H][Nq], natural log
+    void *dq, *dk, *dv;
+    int B, H, Nq, Nkv, d;
+    bool causal;
+    float scale;
+    Elem elem;
+    bool out_f32;
+    float *ws_l2;  // [B*H][Nq] LSE * log2(e)
+    float *ws_dd;  // [B*H][Nq] rowsum(dO * O)
+};
+
 // Query rows handled by one prefill workgroup (depends on d).
 int fwd_rows_per_block(int d);
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+
+// Workspace bytes of the backward: two fp32 values per query row.
+inline std::size_t bwd_workspace_bytes(int B, int H, int Nq)
+{
+    return static_cast<std::size_t>(B) * H * Nq * 2 * sizeof(float);
+}
 
 // Split count used when the caller passes num_splits = 0.
 int decode_auto_splits(int B, int H, int Nkv, int d);

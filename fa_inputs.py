@@ -8,7 +8,8 @@ draw their inputs from here and from nowhere else.
 
 Generator recipe (one independent stream per tensor and head):
     x = default_rng([seed, tensor, b, h]).standard_normal((N, d), float32) * sigma
-with tensor 0 = Q, 1 = K, 2 = V.  The "spike" workload additionally draws, per
+with tensor 0 = Q, 1 = K, 2 = V and 4 = dO (the upstream gradient dL/dO for
+the backward, shaped like Q).  The "spike" workload additionally draws, per
 head, one key index j_h = default_rng([seed, 3, b, h]).integers(0, Nkv) and
 multiplies that K row by 20 before the cast.  Per-head seed sequences make the
 generation order-free, so heads can be produced in parallel or one at a time
@@ -30,7 +31,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-Q, K, V, SPIKE = 0, 1, 2, 3
+Q, K, V, SPIKE, DOUT = 0, 1, 2, 3, 4
 SPIKE_FACTOR = 20.0
 
 
@@ -108,8 +109,8 @@ def f32_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def head_tensor(w: Workload, tensor: int, b: int, h: int) -> np.ndarray:
-    """Bits of one head of Q, K or V: uint16 array of shape (N, d)."""
-    n = w.Nq if tensor == Q else w.Nkv
+    """Bits of one head of Q, K, V or dO: uint16 array of shape (N, d)."""
+    n = w.Nq if tensor in (Q, DOUT) else w.Nkv
     x = normals(w.seed, tensor, b, h, n, w.d)
     if tensor in (Q, K) and w.sigma_qk != 1.0:
         x *= np.float32(w.sigma_qk)
@@ -120,7 +121,7 @@ def head_tensor(w: Workload, tensor: int, b: int, h: int) -> np.ndarray:
 
 def make_tensor(w: Workload, tensor: int, threads: int | None = None) -> np.ndarray:
     """Bits of a whole tensor, uint16 array of shape (B, H, N, d), heads drawn in parallel."""
-    n = w.Nq if tensor == Q else w.Nkv
+    n = w.Nq if tensor in (Q, DOUT) else w.Nkv
     out = np.empty((w.B, w.H, n, w.d), dtype=np.uint16)
 
     def one(bh):

@@ -81,7 +81,7 @@ extern "C" {
 /* HIP's opaque stream handle (identical to the typedef in hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define FA355_VERSION 1
+#define FA355_VERSION 2
 
 /* Element type of q, k, v (and of o unless FA_OUT_F32 is set). */
 enum fa_dtype {
@@ -96,7 +96,7 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID = 1,     /* a precondition above is violated */
     FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. d = 96) */
-    FA_ERR_WORKSPACE = 3,   /* fa_decode workspace missing, misaligned or too small */
+    FA_ERR_WORKSPACE = 3,   /* fa_decode / fa_bwd workspace missing, misaligned or too small */
     FA_ERR_HIP = 4          /* the HIP runtime reported an error (see fa_last_error) */
 };
 
@@ -138,6 +138,41 @@ size_t fa_decode_workspace_size(int B, int H, int Nkv, int d, int num_splits);
 
 /* The split count fa_decode uses for num_splits = 0 (0 if the arguments are invalid). */
 int fa_decode_num_splits(int B, int H, int Nkv, int d);
+
+/*
+ * Backward of fa_fwd: gradients dq, dk, dv of a loss L given dout = dL/do.
+ * The forward keeps only its per-row statistics (LSE) rather than the softmax
+ * matrix, and the backward recomputes the probabilities tile by tile from
+ * them, again without writing an Nq x Nkv matrix to device memory
+ * ("FlashAttention 1-2-3 ...", section "FlashAttention-1: Tiling,
+ * Recomputation, and Online Softmax"; "Flash Attention -- Module 12.3",
+ * section "Training": the backward is IO-aware too).  With z = scale * q.k and
+ * P = exp(z - LSE), the chain rule through the definition gives
+ *
+ *     dv = P^T dout,   dP = dout v^T,   D_i = sum_c dout[i][c] o[i][c],
+ *     dS = P * (dP - D),   dq = scale * dS k,   dk = scale * dS^T q.
+ *
+ * Inputs: q, k, v, o (the forward's output, in the input element type), dout
+ * (like o) and lse (float32 [B][H][Nq], the forward's), all with the layouts
+ * and the causal rule above.  Outputs: dq like q, dk and dv like k, in the
+ * input element type or float32 with FA_OUT_F32.  The same q, k, v, causal
+ * and scale as the forward call must be passed.
+ *
+ * workspace: caller-owned device memory of at least
+ * fa_bwd_workspace_size(B, H, Nq) bytes (two float32 values per query row),
+ * 16-byte aligned, not overlapping any other argument; contents ignored on
+ * entry, unspecified on return; calls sharing it must be ordered on one
+ * stream.  A missing, misaligned or short workspace returns FA_ERR_WORKSPACE.
+ * dq, dk, dv must not overlap any input or each other.  Deterministic (no
+ * atomics): the key-block and query-block passes each recompute P.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+           const float *lse, void *dq, void *dk, void *dv,
+           int B, int H, int Nq, int Nkv, int d, int causal, float scale, int dtype,
+           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace fa_bwd needs (0 if the arguments are invalid). */
+size_t fa_bwd_workspace_size(int B, int H, int Nq);
 
 /* Static, human-readable name of a status code. */
 const char *fa_status_str(int status);

@@ -21,6 +21,10 @@ C = 3 << 32
 O = 4 << 32
 L = 5 << 32
 W = 6 << 32
+DO_ = 7 << 32
+GQ = 8 << 32
+GK = 9 << 32
+GV = 10 << 32
 
 
 def declared_functions():
@@ -31,8 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "fa_decode", "fa_decode_num_splits", "fa_decode_workspace_size", "fa_fwd",
-        "fa_last_error", "fa_status_str", "fa_version"])
+        "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_num_splits", "fa_decode_workspace_size",
+        "fa_fwd", "fa_last_error", "fa_status_str", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -43,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_version() == 1
+    assert fa.fa_version() == 2
     assert [fa.fa_status_str(s) for s in range(5)] == [
         "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP"]
     assert fa.fa_status_str(99) == "FA_ERR_UNKNOWN"
@@ -148,3 +152,48 @@ def test_last_error_is_per_thread():
     t.join()
     assert seen["msg"] == ""
     assert "d=96" in fa.fa_last_error()
+
+
+def bwd(q=A, k=B_, v=C, o=O, dout=DO_, lse=L, dq=GQ, dk=GK, dv=GV, B=1, H=2, Nq=64, Nkv=96, d=128, causal=1,
+        scale=0.125, dtype=fa.FA_F16, ws=W, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_size(B, H, Nq)
+    return status_of(fa.fa_bwd, q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, causal, scale, dtype, ws,
+                     ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dout=None), fa.FA_ERR_INVALID, "non-NULL"),
+    (dict(dk=None), fa.FA_ERR_INVALID, "non-NULL"),
+    (dict(lse=None), fa.FA_ERR_INVALID, "lse"),
+    (dict(o=O + 8), fa.FA_ERR_INVALID, "aligned"),
+    (dict(dv=GV + 4), fa.FA_ERR_INVALID, "aligned"),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "d=32"),
+    (dict(dtype=4), fa.FA_ERR_INVALID, "dtype"),
+    (dict(causal=1, Nq=97), fa.FA_ERR_INVALID, "Nq <= Nkv"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID, "finite"),
+    (dict(Nkv=0), fa.FA_ERR_INVALID, "no keys"),
+    (dict(H=-2), fa.FA_ERR_INVALID, "negative"),
+    (dict(dq=A), fa.FA_ERR_INVALID, "dq overlaps q"),
+    (dict(dk=DO_ + 64), fa.FA_ERR_INVALID, "dk overlaps dout"),
+    (dict(dv=GK + 128, dtype=fa.FA_F16 | fa.FA_OUT_F32), fa.FA_ERR_INVALID, "dk overlaps dv"),
+    (dict(dq=L), fa.FA_ERR_INVALID, "dq overlaps lse"),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE, "workspace"),
+    (dict(ws=W + 8), fa.FA_ERR_WORKSPACE, "aligned"),
+    (dict(ws_bytes=8), fa.FA_ERR_WORKSPACE, "hold"),
+    (dict(ws=GV), fa.FA_ERR_WORKSPACE, "workspace overlaps dv"),
+    (dict(B=1, H=1, Nq=64, Nkv=1 << 24, dtype=fa.FA_F16 | fa.FA_OUT_F32), fa.FA_ERR_UNSUPPORTED, "4 GiB"),
+])
+def test_bwd_rejects(kw, status, needle):
+    got, msg = bwd(**kw)
+    assert got == status, (got, msg)
+    assert needle in msg, msg
+
+
+def test_bwd_sizes_and_empty():
+    # two fp32 values per query row
+    assert fa.fa_bwd_workspace_size(2, 3, 100) == 2 * 3 * 100 * 2 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 0) == 0
+    assert fa.fa_bwd_workspace_size(-1, 1, 4) == 0
+    assert bwd(B=0, q=None, k=None, v=None, o=None, dout=None, lse=None, dq=None, dk=None, dv=None, ws=None,
+               ws_bytes=0)[0] == fa.FA_OK

@@ -68,11 +68,17 @@ def kernel_metadata(src, tmp_path):
     return kernels
 
 
-@pytest.mark.parametrize("src", ["fa_fwd.hip", "fa_decode.hip"])
+# Kernels built for one wave per SIMD (their register file is 512 entries);
+# every other kernel must leave room for two.
+ONE_WAVE_PER_SIMD = ("bwd_dkdv_kernelILi128",)
+
+
+@pytest.mark.parametrize("src", ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip"])
 def test_kernels_do_not_spill(src, tmp_path):
     kernels = kernel_metadata(src, tmp_path)
     assert kernels, f"no kernels found in {src}"
     for k in kernels:
         assert int(k["vgpr_spill_count"]) == 0, f"{k['name']} spills {k['vgpr_spill_count']} VGPRs"
         assert int(k["private_segment_fixed_size"]) == 0, f"{k['name']} uses scratch"
-        assert int(k["vgpr_count"]) <= 256, f"{k['name']}: {k['vgpr_count']} VGPRs leave one wave per SIMD"
+        limit = 512 if any(t in k["name"] for t in ONE_WAVE_PER_SIMD) else 256
+        assert int(k["vgpr_count"]) <= limit, f"{k['name']}: {k['vgpr_count']} registers"
