@@ -381,24 +381,28 @@ void bwd_dq_kernel(BwdParams p)
         for (int e = 0; e < 16; ++e) dqacc[dt][e] = 0.f;
     const float cs = p.c;
 
+    // One 64-key tile, as two 32-key halves each taken through S, dP, dS and
+    // its dQ products before the next (half the score registers live at once).
     auto tile = [&](int st, int kv0) {
         const char *SK = reinterpret_cast<const char *>(sk[st]);
         const char *SV = reinterpret_cast<const char *>(sv[st]);
-        // S^T = K Q^T and dP^T = V dO^T (rows: keys in swap23 order; columns: queries)
-        f32x16 s[2] = {}, dp[2] = {};
+        const bool edge = (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
+        // the last key this lane's row sees, relative to the lane's first key of the tile
+        const int lim = (CAUSAL ? min(qrow + off, p.Nkv - 1) : p.Nkv - 1) - kv0 - 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int kk = 0; kk < 2; ++kk) {
+            // keep the next half's operand loads out of this half (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
+            // S^T = K Q^T and dP^T = V dO^T (rows: keys in swap23 order; columns: queries)
+            f32x16 s = {}, dp = {};
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
+            for (int ks = 0; ks < KS; ++ks) {
                 const u32x4 xk = *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ (ks << 5)) + kk * 32 * ROWB);
                 const u32x4 xv = *reinterpret_cast<const u32x4 *>(SV + (va0 ^ (ks << 5)) + kk * 32 * ROWB);
-                s[kk] = mfma32(as<V8>(xk), qf[ks], s[kk]);
-                dp[kk] = mfma32(as<V8>(xv), gf[ks], dp[kk]);
+                s = mfma32(as<V8>(xk), qf[ks], s);
+                dp = mfma32(as<V8>(xv), gf[ks], dp);
             }
-        const bool edge = (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
-        u32x4 dw[2][2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            u32x4 dw[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -407,18 +411,13 @@ void bwd_dq_kernel(BwdParams p)
 #pragma unroll
                     for (int b = 0; b < 2; ++b) {
                         const int e = 8 * u + 2 * j + b;
-                        float pe = fast_exp2(fmaf(s[kk][e], cs, -l2));
-                        if (edge) {
-                            const int kj = kv0 + 32 * kk + 16 * u + 8 * h + 2 * j + b;
-                            if (kj >= p.Nkv || (CAUSAL && kj > qrow + off)) pe = 0.f;
-                        }
-                        dr[b] = pe * (dp[kk][e] - dd);
+                        float pe = fast_exp2(fmaf(s[e], cs, -l2));
+                        if (edge && 32 * kk + 16 * u + 2 * j + b > lim) pe = 0.f;
+                        dr[b] = pe * (dp[e] - dd);
                     }
-                    dw[kk][u][j] = pack2<T>(dr[0], dr[1]);
+                    dw[u][j] = pack2<T>(dr[0], dr[1]);
                 }
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            // dQ^T += K^T dS^T
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -426,8 +425,9 @@ void bwd_dq_kernel(BwdParams p)
                     const uint32_t rowoff = (32 * kk + 16 * u) * ROWB;
                     const u32x2 lo = lds_read_tr16(SK + ((ta0[0] ^ (dt << 6)) + rowoff));
                     const u32x2 hi = lds_read_tr16(SK + ((ta0[1] ^ (dt << 6)) + rowoff));
-                    dqacc[dt] = mfma32(as<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), as<V8>(dw[kk][u]), dqacc[dt]);
+                    dqacc[dt] = mfma32(as<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]}), as<V8>(dw[u]), dqacc[dt]);
                 }
+        }
     };
 
     if (nkb > 0) issue(0, 0);
