@@ -12,11 +12,15 @@ headline value is prefill TFLOP/s (4*B*H*N^2*d FLOPs halved for causal, over
 the mean kernel time); decode is reported in HBM GB/s over its algorithmic
 bytes (K and V once, q, o and lse).  rank 0 prints one JSON line.
 
+Separately from the step, the backward (fa_bwd: dQ, dK, dV from O and LSE,
+with dO from the seeded generator) is timed on the prefill workload and
+reported in its own "backward" object; it is not part of `value`.
+
 The CPU baseline is the fp64 oracle (plain standard attention that
 materialises the score matrix) timed on a sample of the prefill heads on the
 host's cores; it is a reference point, not the target.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
 """
 from __future__ import annotations
 
@@ -122,6 +126,51 @@ def cpu_baseline(w, x, target_s=12.0):
     }
 
 
+def backward_flops(B, H, Nq, Nkv, d, causal):
+    """The usual count for the attention backward: five products (2.5 x the forward)."""
+    return metric_flops(B, H, Nq, Nkv, d, causal) * 5 // 2
+
+
+def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
+    """fa_bwd on workload w (dO from the seeded generator), each call bracketed by HIP events."""
+    import statistics
+
+    import torch
+    dout = fi.bits_to_torch(fi.make_tensor(w, fi.DOUT), w.dtype).to(q.device)
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = fa.fa_bwd_workspace_size(w.B, w.H, w.Nq)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    sp = stream.cuda_stream
+
+    def call():
+        fa.fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal, w.scale, fa.FA_F16
+                  if w.dtype == "f16" else fa.FA_BF16, ws, nbytes, sp)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    mean = statistics.fmean(ms)
+    flops = backward_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
+    return {
+        "workload": w.name,
+        "ms_mean": round(mean, 4),
+        "ms_min": round(min(ms), 4),
+        "flops": flops,
+        "TFLOP/s": round(flops / (mean * 1e-3) / 1e12, 2),
+        "frac_of_mfma_peak": round(flops / (mean * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+        "note": "FLOPs counted as 2.5 x the forward (five products); the kernels do seven "
+                "(S and dP are formed in both the key-block and the query-block pass)",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +182,8 @@ def main():
                     help="time only one half of the step (for profiling; the default is the whole path)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the separate timing of the backward (fa_bwd) on the prefill workload")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -267,6 +318,9 @@ def main():
         "gpu": {"name": props.name, "cus": props.multi_processor_count,
                 "arch": getattr(props, "gcnArchName", "")},
     }
+    if run_prefill and not args.no_bwd:
+        log("backward (fa_bwd) on the prefill workload")
+        result["backward"] = time_backward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
     if args.only != "all":
         result["partial_step"] = args.only
     if not args.no_cpu_baseline:
