@@ -74,6 +74,10 @@ class Oracle:
                                                         ctypes.c_double, ctypes.POINTER(_i64), _i64,
                                                         ctypes.POINTER(_i64), _i64, _dp, _dp, _dp]
         lib.fa_oracle_attention_bwd_sampled.restype = ctypes.c_int
+        _i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.fa_oracle_paged_decode.argtypes = [_dp, _dp, _dp, _i32p, _i32p, _dp, _dp, _i64, _i64, _i64, _i64,
+                                               _i64, _i64, ctypes.c_int, ctypes.c_double]
+        lib.fa_oracle_paged_decode.restype = ctypes.c_int
         lib.fa_oracle_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -172,6 +176,36 @@ class Oracle:
             raise ValueError(f"oracle rejected the call (rc={rc})")
         return dq, dk, dv
 
+    def paged_decode(self, q, k_pages, v_pages, block_table, seq_lens, *, scale: float, layout: str = "hnd",
+                     dtype=None):
+        """Decode over a paged cache: O [B,H,d] and LSE [B,H] in float64.
+
+        q is [B,H,d]; k_pages / v_pages are [num_pages,H,page_size,d] for
+        layout 'hnd' or [num_pages,page_size,H,d] for 'nhd'; block_table is
+        [B,max_pages] and seq_lens [B] (int32).  A sequence of length 0 gets
+        O = 0 and LSE = -inf."""
+        q, k_pages, v_pages = (self._as_f64(t, dtype) for t in (q, k_pages, v_pages))
+        table = np.ascontiguousarray(block_table, dtype=np.int32)
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, H, d = q.shape
+        if layout == "hnd":
+            P, Hk, ps, dk = k_pages.shape
+        elif layout == "nhd":
+            P, ps, Hk, dk = k_pages.shape
+        else:
+            raise ValueError(f"layout must be 'hnd' or 'nhd', got {layout!r}")
+        if (Hk, dk) != (H, d) or v_pages.shape != k_pages.shape or table.ndim != 2 or table.shape[0] != B \
+                or lens.shape != (B,):
+            raise ValueError("shape mismatch")
+        o = np.empty((B, H, d), dtype=np.float64)
+        lse = np.empty((B, H), dtype=np.float64)
+        rc = self.lib.fa_oracle_paged_decode(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(table, ctypes.c_int32),
+                                             _ptr(lens, ctypes.c_int32), _ptr(o), _ptr(lse), B, H, P, ps,
+                                             table.shape[1], d, 0 if layout == "hnd" else 1, float(scale))
+        if rc:
+            raise ValueError(f"oracle rejected the call (rc={rc})")
+        return o, lse
+
     def threads(self) -> int:
         return int(self.lib.fa_oracle_threads())
 
@@ -204,6 +238,11 @@ def attention_bwd(q, k, v, dout, *, causal, scale, dtype=None):
 
 def attention_bwd_sampled(q, k, v, dout, qrows, kcols, *, causal, scale, dtype=None):
     return default().attention_bwd_sampled(q, k, v, dout, qrows, kcols, causal=causal, scale=scale, dtype=dtype)
+
+
+def paged_decode(q, k_pages, v_pages, block_table, seq_lens, *, scale, layout="hnd", dtype=None):
+    return default().paged_decode(q, k_pages, v_pages, block_table, seq_lens, scale=scale, layout=layout,
+                                  dtype=dtype)
 
 
 def threads() -> int:

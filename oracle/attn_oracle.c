@@ -425,3 +425,80 @@ int fa_oracle_attention_bwd_sampled(const double *q, const double *k, const doub
     free(Dv);
     return 0;
 }
+
+/*
+ * Decode over a paged key/value cache, for one query per (batch, head).
+ *
+ * A serving stack keeps the cache in fixed-size pages and a per-sequence block
+ * table; attention treats each page of the cache as a tile ("FlashAttention 1-2-3:
+ * The IO-Aware Revolution in LLM Inference", sections "Integration in Major
+ * Inference Engines" and "Beyond FlashAttention: Future Directions and
+ * Alternatives").  Reading taken here: key j of sequence b is row
+ * (j mod page_size) of page table[b][j / page_size], for j < lens[b]; the
+ * result is the ordinary softmax attention of the sequence's query over those
+ * lens[b] keys, i.e. exactly the dense attention over the gathered cache.
+ *
+ * kpool, vpool hold num_pages pages; layout 0 stores them [page][H][page_size][d]
+ * (one head's slots contiguous), layout 1 [page][page_size][H][d] (one slot's
+ * heads contiguous).  q: [B][H][d]; table: [B][max_pages]; o: [B][H][d];
+ * lse: [B][H].  A sequence with lens[b] == 0 attends to nothing: its o is 0 and
+ * its lse is -infinity (the empty sum's logarithm).
+ *
+ * The pages that sequence b uses are gathered row by row into a dense
+ * [lens[b]][d] copy, then the three passes of standard attention run on it.
+ * Returns 0, -1 for invalid arguments (a length outside [0, max_pages *
+ * page_size], a used page outside the pool), -2 if out of memory.
+ */
+int fa_oracle_paged_decode(const double *q, const double *kpool, const double *vpool,
+                           const int32_t *table, const int32_t *lens, double *o, double *lse,
+                           int64_t B, int64_t H, int64_t num_pages, int64_t page_size,
+                           int64_t max_pages, int64_t d, int layout, double scale)
+{
+    if (B < 0 || H < 0 || num_pages < 0 || page_size < 1 || max_pages < 0 || d < 1 ||
+        (layout != 0 && layout != 1))
+        return -1;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t n = lens[b];
+        if (n < 0 || n > max_pages * page_size)
+            return -1;
+        for (int64_t t = 0; t * page_size < n; ++t)
+            if (table[b * max_pages + t] < 0 || table[b * max_pages + t] >= num_pages)
+                return -1;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t n = lens[b];
+        double *kd = (double *)malloc((size_t)(n > 0 ? n : 1) * (size_t)d * sizeof(double));
+        double *vd = (double *)malloc((size_t)(n > 0 ? n : 1) * (size_t)d * sizeof(double));
+        if (!kd || !vd) {
+            free(kd);
+            free(vd);
+            return -2;
+        }
+        for (int64_t h = 0; h < H; ++h) {
+            double *oh = o + (b * H + h) * d;
+            if (n == 0) {
+                for (int64_t c = 0; c < d; ++c)
+                    oh[c] = 0.0;
+                lse[b * H + h] = -INFINITY;
+                continue;
+            }
+            for (int64_t j = 0; j < n; ++j) {
+                const int64_t page = table[b * max_pages + j / page_size];
+                const int64_t slot = j % page_size;
+                const int64_t row = layout == 0 ? (page * H + h) * page_size + slot
+                                                : (page * page_size + slot) * H + h;
+                memcpy(kd + j * d, kpool + row * d, (size_t)d * sizeof(double));
+                memcpy(vd + j * d, vpool + row * d, (size_t)d * sizeof(double));
+            }
+            int rc = head_attention(q + (b * H + h) * d, kd, vd, oh, lse + b * H + h, 1, n, d, 0, scale);
+            if (rc) {
+                free(kd);
+                free(vd);
+                return rc;
+            }
+        }
+        free(kd);
+        free(vd);
+    }
+    return 0;
+}

@@ -444,10 +444,87 @@ def pin_bwd_sampled_matches_full(orc):
         _close(sv, dv[kc], tol=1e-12, what="sampled dV rows")
 
 
+# ---------------------------------------------------------------------------
+# decode over a paged cache
+
+def scatter_pages(rng, kd, vd, lens, page_size, layout, extra_pages=3, garbage=1e3):
+    """Scatter dense caches kd, vd [B,H,Nmax,d] into a shuffled page pool.
+
+    Written independently of the reference's gather: pages are drawn from a
+    random permutation of the pool, the unused pool rows hold V = garbage (and
+    K = 0, so that a wrongly read row gets a weight comparable to the real
+    ones), and table entries past a sequence's last page are -1.  Returns
+    (k_pages, v_pages, block_table)."""
+    B, H, _, d = kd.shape
+    need = [-(-int(n) // page_size) for n in lens]
+    max_pages = max(need + [0]) + 1
+    P = sum(need) + extra_pages
+    perm = rng.permutation(P)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    shape = (P, H, page_size, d) if layout == "hnd" else (P, page_size, H, d)
+    kp = np.zeros(shape, dtype=kd.dtype)
+    vp = np.full(shape, garbage, dtype=vd.dtype)
+    used = 0
+    for b in range(B):
+        for t in range(need[b]):
+            page = perm[used]
+            used += 1
+            table[b, t] = page
+            n_here = min(page_size, int(lens[b]) - t * page_size)
+            rows = slice(t * page_size, t * page_size + n_here)
+            if layout == "hnd":
+                kp[page, :, :n_here] = kd[b, :, rows]
+                vp[page, :, :n_here] = vd[b, :, rows]
+            else:
+                kp[page, :n_here] = kd[b, :, rows].transpose(1, 0, 2)
+                vp[page, :n_here] = vd[b, :, rows].transpose(1, 0, 2)
+    return kp, vp, table
+
+
+def pin_paged_matches_dense(orc):
+    # paging only changes where the keys live: the result is the dense
+    # attention (pinned above) over each sequence's first lens[b] keys
+    for layout in ("hnd", "nhd"):
+        for page_size, lens in ((4, [1, 4, 9, 13]), (1, [3, 1, 2]), (5, [11, 5, 24, 6, 1])):
+            rng = _rng(97 + page_size)
+            B, H, d = len(lens), 3, 8
+            Nmax = max(lens)
+            q = rng.standard_normal((B, H, d))
+            kd = rng.standard_normal((B, H, Nmax, d))
+            vd = rng.standard_normal((B, H, Nmax, d))
+            kp, vp, table = scatter_pages(rng, kd, vd, lens, page_size, layout)
+            scale = 1 / math.sqrt(d)
+            o, lse = orc.paged_decode(q, kp, vp, table, np.array(lens, dtype=np.int32), scale=scale, layout=layout)
+            for b in range(B):
+                for h in range(H):
+                    n = lens[b]
+                    ro, rl = orc.attention(q[b, h][None], kd[b, h, :n], vd[b, h, :n], causal=False, scale=scale)
+                    _close(o[b, h], ro[0], what=f"paged {layout} ps={page_size} O ({b},{h})")
+                    _close(lse[b, h], rl[0], what=f"paged {layout} ps={page_size} LSE ({b},{h})")
+
+
+def pin_paged_empty_and_single(orc):
+    # a sequence with one key returns that key's value row and LSE = its
+    # score; a sequence with no key returns O = 0, LSE = -inf
+    rng = _rng(101)
+    B, H, d, page_size = 3, 2, 4, 2
+    lens = [1, 0, 3]
+    q = rng.standard_normal((B, H, d))
+    kd = rng.standard_normal((B, H, 3, d))
+    vd = rng.standard_normal((B, H, 3, d))
+    for layout in ("hnd", "nhd"):
+        kp, vp, table = scatter_pages(rng, kd, vd, lens, page_size, layout)
+        o, lse = orc.paged_decode(q, kp, vp, table, np.array(lens, dtype=np.int32), scale=0.7, layout=layout)
+        for h in range(H):
+            _close(o[0, h], vd[0, h, 0], what="single key O")
+            _close(lse[0, h], 0.7 * float(q[0, h] @ kd[0, h, 0]), what="single key LSE")
+            assert np.all(o[1, h] == 0.0) and lse[1, h] == -np.inf, (o[1, h], lse[1, h])
+
+
 PINS = [
     pin_widen_f16, pin_widen_bf16, pin_decimal_bruteforce, pin_torch_sdpa, pin_two_key_worked,
     pin_constant_v, pin_q_zero, pin_causal_row0, pin_dominant_score, pin_single_key, pin_bounds,
     pin_linearity, pin_permutation, pin_shift_invariance, pin_merge_identity, pin_rows_match_full,
     pin_head_independence, pin_widened_inputs, pin_bwd_torch_autograd, pin_bwd_finite_difference,
-    pin_bwd_invariants, pin_bwd_sampled_matches_full,
+    pin_bwd_invariants, pin_bwd_sampled_matches_full, pin_paged_matches_dense, pin_paged_empty_and_single,
 ]

@@ -42,6 +42,13 @@ MUTANTS = [
      "acc_k += dS[i * Nkv + j] * dO[i * d + c];"),
     ("sampled backward drops D", "dsij = pij * (dp_ - Dv[i]);", "dsij = pij * dp_;"),
     ("sampled backward row term from the wrong row", "Dv[i] = Di;", "Dv[i] = Di * 0.5;"),
+    ("paged layouts swapped", "const int64_t row = layout == 0 ?", "const int64_t row = layout == 1 ?"),
+    ("paged head offset dropped", "? (page * H + h) * page_size + slot", "? (page * H) * page_size + slot"),
+    ("paged slot shifted by one", "const int64_t slot = j % page_size;",
+     "const int64_t slot = (j + 1) % page_size;"),
+    ("paged values gathered from the key pool", "memcpy(vd + j * d, vpool + row * d",
+     "memcpy(vd + j * d, kpool + row * d"),
+    ("paged empty sequence LSE", "lse[b * H + h] = -INFINITY;", "lse[b * H + h] = 0.0;"),
 ]
 
 
