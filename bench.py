@@ -14,13 +14,15 @@ bytes (K and V once, q, o and lse).  rank 0 prints one JSON line.
 
 Separately from the step, the backward (fa_bwd: dQ, dK, dV from O and LSE,
 with dO from the seeded generator) is timed on the prefill workload and
-reported in its own "backward" object; it is not part of `value`.
+reported in its own "backward" object, and decode over a paged cache
+(fa_decode_paged: the decode cache scattered into a shuffled pool of 16-key
+pages) in a "paged_decode" object; neither is part of `value`.
 
 The CPU baseline is the fp64 oracle (plain standard attention that
 materialises the score matrix) timed on a sample of the prefill heads on the
 host's cores; it is a reference point, not the target.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-paged]
 """
 from __future__ import annotations
 
@@ -42,6 +44,7 @@ PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
 PREFILL = "prefill_8k_d128"
 DECODE = "decode_32k_d128"
+PAGED = "decode_32k_d128_paged16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = {
     "prefill": ["exact_io_aware_65_amd/csrc/fa_fwd.hip", "exact_io_aware_65_amd/csrc/fa_device.hpp"],
@@ -171,6 +174,58 @@ def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
     }
 
 
+def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
+    """fa_decode_paged on workload w: the dense decode cache k, v scattered into a
+    shuffled page pool, each call bracketed by HIP events."""
+    import statistics
+
+    import numpy as np
+    import torch
+    plan = fi.workload_plan(w)
+    kp, vp = fi.scatter_to_pages_torch(k, plan), fi.scatter_to_pages_torch(v, plan)
+    table = torch.from_numpy(plan.block_table).to(q.device)
+    lens = torch.from_numpy(plan.seq_lens).to(q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=q.device)
+    nbytes = fa.fa_decode_workspace_size(w.B, w.H, w.Nkv, w.d, num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    sp = stream.cuda_stream
+    max_pages = plan.block_table.shape[1]
+
+    def call():
+        fa.fa_decode_paged(q, kp, vp, table, lens, o, lse, w.B, w.H, w.d, plan.num_pages, plan.page_size,
+                           max_pages, fa.FA_PAGED_HND, w.Nkv, w.scale, fa.FA_F16, num_splits, ws, nbytes, sp)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    mean = statistics.fmean(ms)
+    keys = int(np.asarray(plan.seq_lens, dtype=np.int64).sum())
+    nbytes_alg = 2 * keys * w.H * w.d * 2 + algorithmic_bytes(w.B, w.H, 1, 0, w.d) + plan.block_table.nbytes + \
+        plan.seq_lens.nbytes
+    gbs = nbytes_alg / (mean * 1e-3) / 1e9
+    return {
+        "workload": w.name,
+        "page_size": plan.page_size,
+        "layout": "hnd",
+        "num_pages": plan.num_pages,
+        "ms_mean": round(mean, 4),
+        "ms_min": round(min(ms), 4),
+        "algorithmic_bytes": nbytes_alg,
+        "GB/s": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "note": "the dense decode cache scattered into a shuffled pool of 16-key pages; bytes are K and V "
+                "once, q, o, lse, the block table and the lengths",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +239,8 @@ def main():
                     help="only run a 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the separate timing of the backward (fa_bwd) on the prefill workload")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the separate timing of decode over a paged cache (fa_decode_paged)")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -321,6 +378,10 @@ def main():
     if run_prefill and not args.no_bwd:
         log("backward (fa_bwd) on the prefill workload")
         result["backward"] = time_backward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
+    if run_decode and not args.no_paged:
+        log("decode over a paged cache (fa_decode_paged)")
+        result["paged_decode"] = time_paged_decode(fa, fi, fi.WORKLOADS[PAGED], dq, dk, dv, stream, args.warmup,
+                                                   args.steps, args.num_splits)
     if args.only != "all":
         result["partial_step"] = args.only
     if not args.no_cpu_baseline:

@@ -12,14 +12,18 @@ from ._binding import (  # noqa: F401
     FA_F16,
     FA_OK,
     FA_OUT_F32,
+    FA_PAGED_HND,
+    FA_PAGED_NHD,
     LIBRARY,
     FaError,
     bwd,
     decode,
+    decode_paged,
     fa_bwd,
     fa_bwd_workspace_size,
     fa_decode,
     fa_decode_num_splits,
+    fa_decode_paged,
     fa_decode_workspace_size,
     fa_fwd,
     fa_last_error,

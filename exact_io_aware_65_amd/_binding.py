@@ -5,10 +5,11 @@ kernels of libfa355.so.  PyTorch supplies device memory and the current
 stream.  The library must have been built (``python -m
 exact_io_aware_65_amd.build``); there is no fallback of any kind.
 
-Thin wrappers with the C names (``fa_fwd``, ``fa_decode``, ``fa_bwd``, ...)
+Thin wrappers with the C names (``fa_fwd``, ``fa_decode``, ``fa_decode_paged``,
+``fa_bwd``, ...)
 take device pointers or tensors and raise :class:`FaError` on a non-OK
-status.  The convenience functions :func:`fwd`, :func:`decode` and
-:func:`bwd` allocate the outputs.
+status.  The convenience functions :func:`fwd`, :func:`decode`,
+:func:`decode_paged` and :func:`bwd` allocate the outputs.
 """
 from __future__ import annotations
 
@@ -22,6 +23,8 @@ FA_F16 = 1
 FA_BF16 = 2
 FA_OUT_F32 = 0x100
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+FA_PAGED_HND = 0  # pages [num_pages, H, page_size, d]
+FA_PAGED_NHD = 1  # pages [num_pages, page_size, H, d]
 
 
 class FaError(RuntimeError):
@@ -49,6 +52,10 @@ def library() -> ctypes.CDLL:
         lib.fa_decode_workspace_size.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i, i, i, i]
         lib.fa_decode_num_splits.restype = i
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.fa_decode_paged.argtypes = [vp, vp, vp, i32p, i32p, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp,
+                                        ctypes.c_size_t, vp]
+        lib.fa_decode_paged.restype = i
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
         lib.fa_bwd.restype = i
         lib.fa_bwd_workspace_size.argtypes = [i, i, i]
@@ -96,6 +103,16 @@ def fa_decode_workspace_size(B, H, Nkv, d, num_splits=0) -> int:
 
 def fa_decode_num_splits(B, H, Nkv, d) -> int:
     return int(library().fa_decode_num_splits(B, H, Nkv, d))
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, B, H, d, num_pages, page_size, max_pages,
+                    layout, max_seq_len, scale, dtype, num_splits, workspace, workspace_bytes, stream=None) -> None:
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    _check(library().fa_decode_paged(_addr(q), _addr(k_pages), _addr(v_pages),
+                                     ctypes.cast(_addr(block_table), i32p), ctypes.cast(_addr(seq_lens), i32p),
+                                     _addr(o), _addr(lse), B, H, d, num_pages, page_size, max_pages, int(layout),
+                                     int(max_seq_len), float(scale), int(dtype), int(num_splits), _addr(workspace),
+                                     int(workspace_bytes), _addr(stream)))
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, causal, scale, dtype, workspace,
@@ -197,6 +214,55 @@ def decode(q, k, v, *, scale=None, num_splits=0, out_dtype=None):
     nbytes = fa_decode_workspace_size(B, H, Nkv, d, num_splits)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, code, num_splits, ws, nbytes, _stream(q.device))
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, layout="hnd", max_seq_len=None, scale=None,
+                 num_splits=0, out_dtype=None):
+    """Decode over a paged cache.
+
+    q [B, H, d]; k_pages / v_pages [num_pages, H, page_size, d] for layout
+    'hnd' or [num_pages, page_size, H, d] for 'nhd'; block_table
+    [B, max_pages] and seq_lens [B] int32 on the device.  max_seq_len bounds
+    seq_lens and sizes the key-range splits; it defaults to the table's
+    capacity max_pages * page_size (a tighter bound splits the work better).
+    Returns (o, lse): o [B, H, d], lse [B, H]."""
+    import torch
+    _check_inputs(q, k_pages, v_pages)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H, d], got {tuple(q.shape)}")
+    B, H, d = q.shape
+    if layout == "hnd":
+        num_pages, Hk, page_size, dk = k_pages.shape
+        code_layout = FA_PAGED_HND
+    elif layout == "nhd":
+        num_pages, page_size, Hk, dk = k_pages.shape
+        code_layout = FA_PAGED_NHD
+    else:
+        raise ValueError(f"layout must be 'hnd' or 'nhd', got {layout!r}")
+    if (Hk, dk) != (H, d) or v_pages.shape != k_pages.shape:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, pages {tuple(k_pages.shape)} / {tuple(v_pages.shape)}")
+    for name, t, shape in (("block_table", block_table, (B, None)), ("seq_lens", seq_lens, (B,))):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device or t.dim() != len(shape) \
+                or t.shape[0] != B:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on q's device with leading dimension B")
+    max_pages = block_table.shape[1]
+    if max_seq_len is None:
+        max_seq_len = max_pages * page_size
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    code = _dtype_code(q)
+    odt = q.dtype
+    if out_dtype is not None and out_dtype != q.dtype:
+        if out_dtype != torch.float32:
+            raise TypeError("out_dtype must be None, q.dtype or torch.float32")
+        code |= FA_OUT_F32
+        odt = torch.float32
+    o = torch.empty((B, H, d), dtype=odt, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    nbytes = fa_decode_workspace_size(B, H, max_seq_len, d, num_splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    fa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, B, H, d, num_pages, page_size, max_pages,
+                    code_layout, max_seq_len, scale, code, num_splits, ws, nbytes, _stream(q.device))
     return o, lse
 
 

@@ -217,6 +217,91 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     return FA_OK;
 }
 
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                    const int32_t *seq_lens, void *o, float *lse, int B, int H, int d, int num_pages,
+                    int page_size, int max_pages, int layout, int max_seq_len, float scale, int dtype,
+                    int num_splits, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    static const char *fn = "fa_decode_paged";
+    fa355::Elem elem;
+    bool out_f32;
+    int rc = parse_dtype(fn, dtype, &elem, &out_f32);
+    if (rc) return rc;
+    if ((rc = check_head_dim(fn, d))) return rc;
+    if (B < 0 || H < 0 || num_pages < 0 || max_pages < 0)
+        return fail(FA_ERR_INVALID, "%s: negative size (B=%d H=%d num_pages=%d max_pages=%d)", fn, B, H, num_pages,
+                    max_pages);
+    if (page_size < 1) return fail(FA_ERR_INVALID, "%s: page_size=%d must be >= 1", fn, page_size);
+    if (layout != FA_PAGED_HND && layout != FA_PAGED_NHD)
+        return fail(FA_ERR_INVALID, "%s: layout=%d is neither FA_PAGED_HND nor FA_PAGED_NHD", fn, layout);
+    if (num_splits < 0) return fail(FA_ERR_INVALID, "%s: num_splits=%d must be >= 0", fn, num_splits);
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "%s: scale must be finite", fn);
+    if (B == 0 || H == 0) return FA_OK;
+    const long long capacity = static_cast<long long>(max_pages) * page_size;
+    if (capacity >= (1LL << 31))
+        return fail(FA_ERR_INVALID, "%s: max_pages * page_size = %lld must be below 2^31", fn, capacity);
+    if (max_seq_len < 1 || max_seq_len > capacity)
+        return fail(FA_ERR_INVALID, "%s: max_seq_len=%d must lie in [1, max_pages * page_size = %lld]", fn,
+                    max_seq_len, capacity);
+    if (num_pages < 1) return fail(FA_ERR_INVALID, "%s: the page pool is empty", fn);
+    if (!q || !k_pages || !v_pages || !o)
+        return fail(FA_ERR_INVALID, "%s: q, k_pages, v_pages and o must be non-NULL", fn);
+    if (misaligned(q, 16) || misaligned(k_pages, 16) || misaligned(v_pages, 16) || misaligned(o, 16))
+        return fail(FA_ERR_INVALID, "%s: q, k_pages, v_pages and o must be 16-byte aligned", fn);
+    if (!block_table || !seq_lens || misaligned(block_table, 4) || misaligned(seq_lens, 4))
+        return fail(FA_ERR_INVALID, "%s: block_table and seq_lens must be non-NULL and 4-byte aligned", fn);
+    if (lse && misaligned(lse, 4)) return fail(FA_ERR_INVALID, "%s: lse must be 4-byte aligned", fn);
+    const unsigned __int128 bh = static_cast<unsigned __int128>(B) * H;
+    const unsigned __int128 pool_el = static_cast<unsigned __int128>(num_pages) * page_size * H * d;
+    if (bh * d >= kMaxElems || pool_el >= kMaxElems)
+        return fail(FA_ERR_INVALID, "%s: tensor sizes exceed 2^62 elements", fn);
+
+    int splits, chunk;
+    resolve_splits(B, H, max_seq_len, d, num_splits, &splits, &chunk);
+    const long long blocks = static_cast<long long>(B) * H * splits;
+    if (blocks > 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+    const size_t need = fa355::decode_workspace_bytes(B, H, splits, d);
+    if (!workspace || misaligned(workspace, 16) || workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)",
+                    fn, need, workspace_bytes, workspace);
+    const Span ins[5] = {span("q", q, bh * d * 2), span("k_pages", k_pages, pool_el * 2),
+                         span("v_pages", v_pages, pool_el * 2),
+                         span("block_table", block_table, static_cast<unsigned __int128>(B) * max_pages * 4),
+                         span("seq_lens", seq_lens, static_cast<unsigned __int128>(B) * 4)};
+    const Span outs[2] = {span("o", o, bh * d * (out_f32 ? 4 : 2)), span("lse", lse, lse ? bh * 4 : 0)};
+    for (const Span &os : outs) {
+        if (os.hi <= os.lo) continue;
+        for (const Span &is : ins)
+            if (is.hi > is.lo && overlap(os, is)) return fail(FA_ERR_INVALID, "%s: %s overlaps %s", fn, os.name, is.name);
+    }
+    if (outs[1].hi > outs[1].lo && overlap(outs[0], outs[1])) return fail(FA_ERR_INVALID, "%s: lse overlaps o", fn);
+    const Span ws = span("workspace", workspace, need);
+    for (const Span &s : ins)
+        if (s.hi > s.lo && overlap(ws, s)) return fail(FA_ERR_WORKSPACE, "%s: workspace overlaps %s", fn, s.name);
+    for (const Span &s : outs)
+        if (s.hi > s.lo && overlap(ws, s)) return fail(FA_ERR_WORKSPACE, "%s: workspace overlaps %s", fn, s.name);
+
+    float *ws_o = static_cast<float *>(workspace);
+    float *ws_lse = ws_o + static_cast<size_t>(B) * H * splits * d;
+    fa355::DecodeArgs a{q, k_pages, v_pages, o, lse, B, H, max_seq_len, d, scale, elem, out_f32, splits, chunk,
+                        ws_o, ws_lse};
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.num_pages = num_pages;
+    a.page_size = page_size;
+    a.max_pages = max_pages;
+    a.layout = layout;
+    if (log_enabled())
+        std::fprintf(stderr,
+                     "fa355: fa_decode_paged B=%d H=%d d=%d pages=%d page_size=%d max_pages=%d layout=%d "
+                     "max_seq_len=%d dtype=0x%x splits=%d chunk=%d\n",
+                     B, H, d, num_pages, page_size, max_pages, layout, max_seq_len, dtype, splits, chunk);
+    const hipError_t err = fa355::launch_decode(a, stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return FA_OK;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int Nq)
 {
     if (B < 0 || H < 0 || Nq < 0) return 0;

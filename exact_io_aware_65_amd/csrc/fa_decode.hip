@@ -16,12 +16,23 @@
 // and the chunk's normalised partial output and base-2 log-sum-exp go to the
 // workspace.
 //
+// The paged variant reads the cache through a block table: sequence b's key
+// j sits in page block_table[b][j / page_size], slot j % page_size, of a pool
+// of pages laid out [page][H][slot][d] or [page][slot][H][d] -- the cache of
+// serving stacks that allocate it in fixed-size pages, each page one tile of
+// the attention ("FlashAttention 1-2-3 ...", sections "Integration in Major
+// Inference Engines" and "Beyond FlashAttention").  Each sequence has its own
+// length (seq_lens[b], read on the device and clamped to the host's bound
+// max_seq_len); chunks past it are empty and carry weight 0 into the combine.
+//
 // Pass 2 (combine kernel): per head, the partial results are merged exactly
 // by their log-sum-exp values, the two-block merge of "FlashAttention 1-2-3
 // ...", section "The Math Behind the Online Softmax Trick", applied to all
 // chunks at once: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
+
+#include <type_traits>
 
 namespace fa355 {
 namespace {
@@ -34,9 +45,53 @@ struct SplitParams {
     float *ws_o, *ws_lse;
     int Nkv, chunk, splits;
     float scale_log2;
+    // paged cache only
+    const int *block_table;  // [B][max_pages] page indices
+    const int *seq_lens;     // [B] keys cached per sequence
+    int H, num_pages, page_size, max_pages, max_len;
+    unsigned div_magic;      // key / page_size == (key * div_magic) >> div_shift for key < 2^31
+    int div_shift;
+    size_t page_stride, head_stride, slot_stride;  // elements
 };
 
-template <int D, typename T>
+// Element offset of key `key` of head bh in a contiguous [B*H][Nkv][D] cache.
+template <int D> struct DenseRows {
+    size_t base;
+    __device__ DenseRows(const SplitParams &p, int bh) : base(static_cast<size_t>(bh) * p.Nkv * D) {}
+    __device__ size_t operator()(int key) const { return base + static_cast<size_t>(key) * D; }
+};
+
+// Element offset of key `key` of head bh in a paged cache: the page comes
+// from the sequence's row of the block table, the slot is key mod page_size.
+// Page indices are clamped to the pool, so a bad table reads wrong rows but
+// never outside it.  The division by the page size is a multiply-high by a
+// magic number (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): with l = ceil(log2 page_size) and
+// m = ceil(2^(31+l) / page_size) < 2^32, floor(key * m / 2^(31+l)) is exact
+// for every key < 2^31, because the rounding of m adds less than
+// key / 2^(31+l) < 1 / page_size to key / page_size.
+template <int D> struct PagedRows {
+    const int *table;
+    size_t head_base, page_stride, slot_stride;
+    unsigned magic;
+    int shift, page_size, last_page;
+    __device__ PagedRows(const SplitParams &p, int bh)
+        : table(p.block_table + static_cast<size_t>(bh / p.H) * p.max_pages),
+          head_base(static_cast<size_t>(bh % p.H) * p.head_stride), page_stride(p.page_stride),
+          slot_stride(p.slot_stride), magic(p.div_magic), shift(p.div_shift), page_size(p.page_size),
+          last_page(p.num_pages - 1)
+    {
+    }
+    __device__ size_t operator()(int key) const
+    {
+        const int t = static_cast<int>((static_cast<unsigned long long>(static_cast<unsigned>(key)) * magic) >> shift);
+        const int slot = key - t * page_size;
+        const int page = min(max(table[t], 0), last_page);
+        return head_base + static_cast<size_t>(page) * page_stride + static_cast<size_t>(slot) * slot_stride;
+    }
+};
+
+template <int D, typename T, bool PAGED>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParams p)
 {
     constexpr int LPK = D / 8;                 // lanes per key row
@@ -50,11 +105,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParam
     const int g = lane / LPK, r = lane % LPK;
     const int grp = w * KPI + g;
     const int ks = split * p.chunk;
-    const int ke = min(p.Nkv, ks + p.chunk);
+    int n = p.Nkv;  // keys of this sequence
+    if constexpr (PAGED) n = min(max(p.seq_lens[bh / p.H], 0), p.max_len);
+    const int ke = min(n, ks + p.chunk);  // ke <= ks: a chunk past the sequence's end (empty)
+    using Rows = typename std::conditional<PAGED, PagedRows<D>, DenseRows<D>>::type;
+    const Rows row_of(p, bh);
 
-    const size_t kvbase = static_cast<size_t>(bh) * p.Nkv * D + 8 * r;
-    const T *Kg = static_cast<const T *>(p.k) + kvbase;
-    const T *Vg = static_cast<const T *>(p.v) + kvbase;
+    const T *Kg = static_cast<const T *>(p.k) + 8 * r;
+    const T *Vg = static_cast<const T *>(p.v) + 8 * r;
     const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const T *>(p.q) + static_cast<size_t>(bh) * D + 8 * r);
 
     float m = -INFINITY, l = 0.f;
@@ -69,8 +127,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParam
             const int key = base + u * GROUPS + grp;
             u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
             if (key < ke) {
-                kx = *reinterpret_cast<const u32x4 *>(Kg + static_cast<size_t>(key) * D);
-                vx = *reinterpret_cast<const u32x4 *>(Vg + static_cast<size_t>(key) * D);
+                const size_t row = row_of(key);
+                kx = *reinterpret_cast<const u32x4 *>(Kg + row);
+                vx = *reinterpret_cast<const u32x4 *>(Vg + row);
             }
             kr[u] = kx;
             vr[u] = vx;
@@ -126,8 +185,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParam
             o += s_acc[G][tid] * wgt;
         }
         const size_t slot = static_cast<size_t>(bh) * p.splits + split;
-        p.ws_o[slot * D + tid] = o / L;
-        if (tid == 0) p.ws_lse[slot] = M + __builtin_amdgcn_logf(L);
+        // an empty chunk (paged: past the sequence's end) contributes weight 0
+        p.ws_o[slot * D + tid] = L > 0.f ? o / L : 0.f;
+        if (tid == 0) p.ws_lse[slot] = L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;
     }
 }
 
@@ -146,21 +206,24 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(CombineParams p)
     const float *O = p.ws_o + static_cast<size_t>(bh) * p.splits * D + d;
     float M = -INFINITY;
     for (int s = 0; s < p.splits; ++s) M = fmaxf(M, L[s]);
+    const float Mref = M == -INFINITY ? 0.f : M;  // every chunk empty: O = 0/0 below
     float den = 0.f, num = 0.f;
     for (int s = 0; s < p.splits; ++s) {
-        const float wgt = fast_exp2(L[s] - M);
+        const float wgt = fast_exp2(L[s] - Mref);
         den += wgt;
         num += wgt * O[static_cast<size_t>(s) * D];
     }
-    static_cast<TO *>(p.o)[static_cast<size_t>(bh) * D + d] = static_cast<TO>(num / den);
-    if (d == 0 && p.lse) p.lse[bh] = (M + __builtin_amdgcn_logf(den)) * kLn2;
+    // den == 0 only when every chunk was empty (a paged sequence of length 0):
+    // attention over no key gives O = 0 and LSE = ln 0 = -inf
+    static_cast<TO *>(p.o)[static_cast<size_t>(bh) * D + d] = static_cast<TO>(den > 0.f ? num / den : 0.f);
+    if (d == 0 && p.lse) p.lse[bh] = den > 0.f ? (M + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
 }
 
-template <int D, typename T>
+template <int D, typename T, bool PAGED>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream)
 {
     const int n_bh = a.B * a.H;
-    SplitParams sp;
+    SplitParams sp{};
     sp.q = a.q;
     sp.k = a.k;
     sp.v = a.v;
@@ -170,8 +233,25 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream)
     sp.chunk = a.chunk;
     sp.splits = a.splits;
     sp.scale_log2 = a.scale * kLog2e;
+    sp.block_table = a.block_table;
+    sp.seq_lens = a.seq_lens;
+    sp.H = a.H;
+    sp.num_pages = a.num_pages;
+    sp.page_size = a.page_size;
+    sp.max_pages = a.max_pages;
+    sp.max_len = a.Nkv;
+    if (PAGED) {
+        int l = 0;
+        while ((1LL << l) < a.page_size) ++l;
+        sp.div_magic = static_cast<unsigned>(((1ULL << (31 + l)) + a.page_size - 1) / a.page_size);
+        sp.div_shift = 31 + l;
+        const size_t ps = static_cast<size_t>(a.page_size), H = static_cast<size_t>(a.H);
+        sp.page_stride = ps * H * D;
+        sp.head_stride = a.layout == 0 ? ps * D : D;
+        sp.slot_stride = a.layout == 0 ? D : H * D;
+    }
     const dim3 grid1(static_cast<unsigned>(static_cast<long long>(n_bh) * a.splits));
-    hipLaunchKernelGGL((decode_split_kernel<D, T>), grid1, dim3(64 * kDecWaves), 0, stream, sp);
+    hipLaunchKernelGGL((decode_split_kernel<D, T, PAGED>), grid1, dim3(64 * kDecWaves), 0, stream, sp);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
@@ -191,7 +271,9 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream)
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 {
-    return a.elem == Elem::F16 ? launch<D, _Float16>(a, stream) : launch<D, __bf16>(a, stream);
+    if (a.block_table)
+        return a.elem == Elem::F16 ? launch<D, _Float16, true>(a, stream) : launch<D, __bf16, true>(a, stream);
+    return a.elem == Elem::F16 ? launch<D, _Float16, false>(a, stream) : launch<D, __bf16, false>(a, stream);
 }
 
 }  // namespace

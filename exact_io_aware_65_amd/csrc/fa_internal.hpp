@@ -35,6 +35,12 @@ struct DecodeArgs {
     int chunk;       // keys per split (the last split may hold fewer)
     float *ws_o;     // [B*H][splits][d] normalised partial outputs
     float *ws_lse;   // [B*H][splits] partial log2-sum-exp values
+    // paged cache (block_table non-null): k, v are pools of num_pages pages,
+    // [page][H][slot][d] (layout 0) or [page][slot][H][d] (layout 1); Nkv is
+    // then the bound on seq_lens that sized the splits
+    const int *block_table = nullptr;  // [B][max_pages]
+    const int *seq_lens = nullptr;     // [B]
+    int num_pages = 0, page_size = 0, max_pages = 0, layout = 0;
 };
 
 struct BwdArgs {

@@ -21,6 +21,15 @@ Inference", section "When FlashAttention Doesn't Help", and the
 B, H, T, D = 2, 8, 2048, 64 causal call in "Flash Attention — Module 12.3",
 section "Using Scaled Dot-Product Attention in PyTorch".  Decode (one query
 against a long cache) is the T_q = 1 case of that page's "Prefill vs Decode".
+
+Paged caches (a page pool plus a block table, the storage of serving stacks
+named in "FlashAttention 1-2-3 ...", section "Integration in Major Inference
+Engines") are synthetic too: default_rng([seed, 5]) draws the sequence
+lengths (all Nkv, or uniform in [1, Nkv] when ragged) and then a random
+permutation of the pool, whose pages are handed out in that order, sequence
+by sequence -- the fragmented free list of a long-running server.  The dense
+K and V above are scattered into the pages, so a paged workload holds the
+same key and value bits as its dense twin.
 """
 from __future__ import annotations
 
@@ -31,7 +40,7 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-Q, K, V, SPIKE, DOUT = 0, 1, 2, 3, 4
+Q, K, V, SPIKE, DOUT, PAGES = 0, 1, 2, 3, 4, 5
 SPIKE_FACTOR = 20.0
 
 
@@ -50,6 +59,8 @@ class Workload:
     spike: bool = False    # one K row per head multiplied by SPIKE_FACTOR
     out_f32: bool = False  # O written as float32 instead of the input type
     decode: bool = False   # one query per (b, h) against the whole cache
+    page_size: int = 0     # > 0: the decode cache is paged (see paged_plan)
+    ragged: bool = False   # paged: per-sequence lengths drawn in [1, Nkv]
 
     @property
     def scale(self) -> float:
@@ -77,6 +88,8 @@ WORKLOADS = {
                  dtype="bf16", causal=True, seed=3, spike=True),
         Workload("decode_32k_d128", B=16, H=32, Nq=1, Nkv=32768, d=128, dtype="f16",
                  causal=False, seed=4, decode=True),
+        Workload("decode_32k_d128_paged16", B=16, H=32, Nq=1, Nkv=32768, d=128, dtype="f16",
+                 causal=False, seed=4, decode=True, page_size=16),
     ]
 }
 
@@ -169,3 +182,80 @@ def torch_to_bits(t) -> np.ndarray:
     """Bit patterns of a 16-bit CPU torch tensor as uint16."""
     import torch
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# paged caches
+
+@dataclass(frozen=True)
+class PagedPlan:
+    """Where each sequence's keys live in a pool of pages."""
+    page_size: int
+    seq_lens: np.ndarray     # int32 [B]
+    block_table: np.ndarray  # int32 [B, max_pages]; -1 past a sequence's last page
+    num_pages: int
+
+
+def paged_plan(seed: int, B: int, max_len: int, page_size: int, ragged: bool = False,
+               spare_pages: int = 0, lens=None) -> PagedPlan:
+    """Seeded lengths and a shuffled page assignment (see the module docstring).
+
+    lens, if given, fixes the lengths instead of drawing them; spare_pages
+    adds pool pages that no sequence uses."""
+    rng = np.random.default_rng([seed, PAGES])
+    if lens is not None:
+        seq = np.asarray(lens, dtype=np.int64)
+    elif ragged:
+        seq = rng.integers(1, max_len + 1, B)
+    else:
+        seq = np.full(B, max_len, dtype=np.int64)
+    need = -(-seq // page_size)
+    max_pages = max(1, -(-max_len // page_size))
+    num_pages = int(need.sum()) + spare_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    start = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[start:start + need[b]]
+        start += int(need[b])
+    return PagedPlan(page_size, seq.astype(np.int32), table, num_pages)
+
+
+def workload_plan(w: Workload) -> PagedPlan:
+    return paged_plan(w.seed, w.B, w.Nkv, w.page_size, ragged=w.ragged)
+
+
+def scatter_to_pages(x: np.ndarray, plan: PagedPlan, layout: str = "hnd", fill: int = 0) -> np.ndarray:
+    """Dense [B, H, N, d] cache -> page pool ([P, H, ps, d] 'hnd' or [P, ps, H, d] 'nhd').
+
+    Slots that hold no key of any sequence are set to the bit pattern fill."""
+    B, H, N, d = x.shape
+    ps = plan.page_size
+    shape = (plan.num_pages, H, ps, d) if layout == "hnd" else (plan.num_pages, ps, H, d)
+    pool = np.full(shape, fill, dtype=x.dtype)
+    for b in range(B):
+        n = int(plan.seq_lens[b])
+        for t in range(-(-n // ps)):
+            rows = min(ps, n - t * ps)
+            src = x[b, :, t * ps:t * ps + rows]
+            if layout == "hnd":
+                pool[plan.block_table[b, t], :, :rows] = src
+            else:
+                pool[plan.block_table[b, t], :rows] = src.transpose(1, 0, 2)
+    return pool
+
+
+def scatter_to_pages_torch(x, plan: PagedPlan, layout: str = "hnd"):
+    """scatter_to_pages for a device tensor x [B, H, N, d] whose lengths are all N
+    and N a multiple of the page size (the benchmark's paged workload)."""
+    import torch
+    B, H, N, d = x.shape
+    ps = plan.page_size
+    if N % ps or not (plan.seq_lens == N).all():
+        raise ValueError("scatter_to_pages_torch needs full sequences of whole pages")
+    tiles = x.view(B, H, N // ps, ps, d)
+    tiles = tiles.permute(0, 2, 1, 3, 4) if layout == "hnd" else tiles.permute(0, 2, 3, 1, 4)
+    pool = torch.empty((plan.num_pages,) + tuple(tiles.shape[2:]), dtype=x.dtype, device=x.device)
+    idx = torch.from_numpy(plan.block_table[:, :N // ps].reshape(-1).astype(np.int64)).to(x.device)
+    pool[idx] = tiles.reshape((-1,) + tuple(tiles.shape[2:]))
+    return pool

@@ -73,6 +73,7 @@
 #define FA355_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -81,7 +82,7 @@ extern "C" {
 /* HIP's opaque stream handle (identical to the typedef in hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define FA355_VERSION 2
+#define FA355_VERSION 3
 
 /* Element type of q, k, v (and of o unless FA_OUT_F32 is set). */
 enum fa_dtype {
@@ -138,6 +139,50 @@ size_t fa_decode_workspace_size(int B, int H, int Nkv, int d, int num_splits);
 
 /* The split count fa_decode uses for num_splits = 0 (0 if the arguments are invalid). */
 int fa_decode_num_splits(int B, int H, int Nkv, int d);
+
+/* Page layouts of the paged cache (fa_decode_paged's `layout`). */
+enum {
+    FA_PAGED_HND = 0, /* k_pages, v_pages: [num_pages][H][page_size][d]: a head's slots contiguous */
+    FA_PAGED_NHD = 1  /* k_pages, v_pages: [num_pages][page_size][H][d]: a slot's heads contiguous */
+};
+
+/*
+ * Decode over a paged KV cache: fa_decode for B sequences whose keys and
+ * values live in fixed-size pages of a shared pool, located through a block
+ * table, each page being one tile of the attention ("FlashAttention 1-2-3
+ * ...", sections "Integration in Major Inference Engines" and "Beyond
+ * FlashAttention: Future Directions and Alternatives").  Key j < seq_lens[b]
+ * of sequence b is slot j % page_size of page block_table[b][j / page_size];
+ * O and LSE are the attention of q[b][h] over those seq_lens[b] keys, exactly
+ * as fa_decode computes it over a contiguous cache.
+ *
+ *   q, o          [B][H][d] (o in q's type, or fp32 with FA_OUT_F32); lse [B][H] or NULL
+ *   k_pages,
+ *   v_pages       num_pages pages in `layout` (FA_PAGED_HND or FA_PAGED_NHD), q's type
+ *   block_table   [B][max_pages] int32 page indices, device memory
+ *   seq_lens      [B] int32 key counts, device memory
+ *   max_seq_len   a host-side bound on seq_lens, 1 <= max_seq_len <= max_pages * page_size;
+ *                 it sizes the key-range splits exactly as Nkv does for fa_decode
+ *
+ * block_table and seq_lens are read on the device, so the library cannot
+ * check them: a length outside [0, max_seq_len] is clamped into it, and a
+ * page index outside [0, num_pages) is clamped into the pool, so a bad table
+ * yields wrong values but no access outside the arguments.  Table entries
+ * past a sequence's last page are never read.  A sequence of length 0 gets
+ * O = 0 and LSE = -infinity.  page_size may be any value >= 1, and
+ * max_pages * page_size must stay below 2^31.
+ *
+ * workspace: as for fa_decode, fa_decode_workspace_size(B, H, max_seq_len, d,
+ * num_splits) bytes.  q, k_pages, v_pages, o and workspace must be 16-byte
+ * aligned, block_table, seq_lens and lse 4-byte aligned; o and lse must not
+ * overlap any input.  Errors: FA_ERR_INVALID for bad sizes, layout, pointers
+ * or overlaps; FA_ERR_UNSUPPORTED for d not in {64, 128}; FA_ERR_WORKSPACE as
+ * for fa_decode.
+ */
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                    const int32_t *seq_lens, void *o, float *lse, int B, int H, int d, int num_pages,
+                    int page_size, int max_pages, int layout, int max_seq_len, float scale, int dtype,
+                    int num_splits, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Backward of fa_fwd: gradients dq, dk, dv of a loss L given dout = dL/do.

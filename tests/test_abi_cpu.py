@@ -35,8 +35,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_num_splits", "fa_decode_workspace_size",
-        "fa_fwd", "fa_last_error", "fa_status_str", "fa_version"])
+        "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_num_splits", "fa_decode_paged",
+        "fa_decode_workspace_size", "fa_fwd", "fa_last_error", "fa_status_str", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_version() == 2
+    assert fa.fa_version() == 3
     assert [fa.fa_status_str(s) for s in range(5)] == [
         "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP"]
     assert fa.fa_status_str(99) == "FA_ERR_UNKNOWN"
@@ -121,6 +121,58 @@ def test_decode_rejects(kw, status, needle):
     got, msg = dec(**kw)
     assert got == status, (got, msg)
     assert needle in msg, msg
+
+
+TB = 11 << 32
+SL = 12 << 32
+
+
+def paged(q=A, kp=B_, vp=C, table=TB, lens=SL, o=O, lse=L, B=2, H=2, d=128, num_pages=64, page_size=16,
+          max_pages=32, layout=fa.FA_PAGED_HND, max_seq_len=None, scale=0.1, dtype=fa.FA_F16, splits=0, ws=W,
+          ws_bytes=None):
+    if max_seq_len is None:
+        max_seq_len = max_pages * page_size
+    if ws_bytes is None:
+        ws_bytes = fa.fa_decode_workspace_size(B, H, max(max_seq_len, 1), d, splits)
+    return status_of(fa.fa_decode_paged, q, kp, vp, table, lens, o, lse, B, H, d, num_pages, page_size, max_pages,
+                     layout, max_seq_len, scale, dtype, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED, "d=96"),
+    (dict(dtype=5), fa.FA_ERR_INVALID, "dtype"),
+    (dict(page_size=0), fa.FA_ERR_INVALID, "page_size"),
+    (dict(layout=2), fa.FA_ERR_INVALID, "layout"),
+    (dict(num_pages=-1), fa.FA_ERR_INVALID, "negative"),
+    (dict(num_pages=0), fa.FA_ERR_INVALID, "pool is empty"),
+    (dict(max_seq_len=0), fa.FA_ERR_INVALID, "max_seq_len"),
+    (dict(max_seq_len=32 * 16 + 1), fa.FA_ERR_INVALID, "max_seq_len"),
+    (dict(max_pages=1 << 20, page_size=1 << 11, max_seq_len=100), fa.FA_ERR_INVALID, "2^31"),
+    (dict(splits=-2), fa.FA_ERR_INVALID, "num_splits"),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID, "finite"),
+    (dict(table=None), fa.FA_ERR_INVALID, "block_table"),
+    (dict(lens=SL + 2), fa.FA_ERR_INVALID, "4-byte"),
+    (dict(kp=B_ + 8), fa.FA_ERR_INVALID, "16-byte"),
+    (dict(o=None), fa.FA_ERR_INVALID, "non-NULL"),
+    (dict(lse=L + 1), fa.FA_ERR_INVALID, "aligned"),
+    (dict(o=B_ + 4096), fa.FA_ERR_INVALID, "o overlaps k_pages"),
+    (dict(lse=TB), fa.FA_ERR_INVALID, "lse overlaps block_table"),
+    (dict(lse=O), fa.FA_ERR_INVALID, "lse overlaps o"),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE, "workspace"),
+    (dict(ws_bytes=64), fa.FA_ERR_WORKSPACE, "hold"),
+    (dict(ws=SL - 64), fa.FA_ERR_WORKSPACE, "workspace overlaps seq_lens"),
+])
+def test_decode_paged_rejects(kw, status, needle):
+    got, msg = paged(**kw)
+    assert got == status, (got, msg)
+    assert needle in msg, msg
+
+
+def test_decode_paged_empty_is_noop():
+    assert paged(B=0, q=None, kp=None, vp=None, table=None, lens=None, o=None, lse=None, ws=None,
+                 ws_bytes=0)[0] == fa.FA_OK
+    assert paged(H=0, q=None, kp=None, vp=None, table=None, lens=None, o=None, lse=None, ws=None,
+                 ws_bytes=0)[0] == fa.FA_OK
 
 
 def test_decode_sizes():

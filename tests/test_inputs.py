@@ -13,7 +13,9 @@ def test_workload_table():
     assert (w["prefill_8k_d128"].H, w["prefill_8k_d128"].Nq, w["prefill_8k_d128"].sigma_qk) == (32, 8192, 1.5)
     assert w["prefill_16k_d128_bf16"].dtype == "bf16" and w["prefill_16k_d128_bf16"].spike
     assert w["decode_32k_d128"].Nq == 1 and w["decode_32k_d128"].Nkv == 32768 and w["decode_32k_d128"].decode
-    assert [x.seed for x in w.values()] == [0, 1, 2, 3, 4]
+    assert [x.seed for x in w.values()] == [0, 1, 2, 3, 4, 4]
+    assert w["decode_32k_d128_paged16"].page_size == 16 and w["decode_32k_d128_paged16"].with_(
+        name="decode_32k_d128", page_size=0) == w["decode_32k_d128"]
     assert w["prefill_8k_d128"].scale == float(np.float32(1 / np.sqrt(128)))
 
 
@@ -65,3 +67,35 @@ def test_bits_roundtrip_torch():
     t = fi.bits_to_torch(bits, "f16")
     assert t.tolist() == [1.0, -2.0, 2.0 ** -24]
     assert np.array_equal(fi.torch_to_bits(t), bits)
+
+
+def test_paged_plan_and_scatter():
+    plan = fi.paged_plan(9, 5, 50, 8, ragged=True, spare_pages=4)
+    assert plan.block_table.shape == (5, 7) and plan.seq_lens.dtype == np.int32
+    assert ((1 <= plan.seq_lens) & (plan.seq_lens <= 50)).all()
+    need = -(-plan.seq_lens // 8)
+    used = np.concatenate([plan.block_table[b, :need[b]] for b in range(5)])
+    # every page is used at most once, the rest of the table is -1
+    assert len(set(used.tolist())) == used.size and plan.num_pages == used.size + 4
+    assert all((plan.block_table[b, need[b]:] == -1).all() for b in range(5))
+    assert np.array_equal(fi.paged_plan(9, 5, 50, 8, ragged=True, spare_pages=4).block_table, plan.block_table)
+    rng = np.random.default_rng(0)
+    x = rng.integers(0, 60000, (5, 3, 50, 4)).astype(np.uint16)
+    for layout in ("hnd", "nhd"):
+        pool = fi.scatter_to_pages(x, plan, layout, fill=0xFFFF)
+        for b in range(5):
+            for j in range(int(plan.seq_lens[b])):
+                page, slot = plan.block_table[b, j // 8], j % 8
+                row = pool[page, :, slot] if layout == "hnd" else pool[page, slot]
+                assert np.array_equal(row, x[b, :, j])
+        assert (pool == 0xFFFF).sum() == 3 * 4 * (plan.num_pages * 8 - int(plan.seq_lens.sum()))
+
+
+def test_scatter_to_pages_torch_matches_numpy():
+    plan = fi.paged_plan(3, 2, 32, 4, spare_pages=2)
+    x = np.random.default_rng(1).integers(0, 60000, (2, 3, 32, 8)).astype(np.uint16)
+    for layout in ("hnd", "nhd"):
+        ref = fi.scatter_to_pages(x, plan, layout)
+        got = fi.scatter_to_pages_torch(torch.from_numpy(x.view(np.int16)), plan, layout).numpy().view(np.uint16)
+        used = np.unique(plan.block_table[plan.block_table >= 0])
+        assert np.array_equal(got[used], ref[used])
