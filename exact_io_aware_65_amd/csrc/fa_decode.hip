@@ -54,11 +54,18 @@ struct SplitParams {
     size_t page_stride, head_stride, slot_stride;  // elements
 };
 
-// Element offset of key `key` of head bh in a contiguous [B*H][Nkv][D] cache.
+// Key-row addressing of head bh, in two steps so that the memory reads of
+// the first (the block table, for a paged cache) can be issued one iteration
+// ahead of their use: ref(key) starts the lookup, offset(ref) gives the
+// row's element offset in the cache.
+//
+// A contiguous [B*H][Nkv][D] cache needs no lookup.
 template <int D> struct DenseRows {
+    using Ref = int;
     size_t base;
     __device__ DenseRows(const SplitParams &p, int bh) : base(static_cast<size_t>(bh) * p.Nkv * D) {}
-    __device__ size_t operator()(int key) const { return base + static_cast<size_t>(key) * D; }
+    __device__ Ref ref(int key) const { return key; }
+    __device__ size_t offset(Ref key) const { return base + static_cast<size_t>(key) * D; }
 };
 
 // Element offset of key `key` of head bh in a paged cache: the page comes
@@ -71,6 +78,9 @@ template <int D> struct DenseRows {
 // for every key < 2^31, because the rounding of m adds less than
 // key / 2^(31+l) < 1 / page_size to key / page_size.
 template <int D> struct PagedRows {
+    struct Ref {
+        int page, slot;
+    };
     const int *table;
     size_t head_base, page_stride, slot_stride;
     unsigned magic;
@@ -82,12 +92,15 @@ template <int D> struct PagedRows {
           last_page(p.num_pages - 1)
     {
     }
-    __device__ size_t operator()(int key) const
+    __device__ Ref ref(int key) const
     {
         const int t = static_cast<int>((static_cast<unsigned long long>(static_cast<unsigned>(key)) * magic) >> shift);
-        const int slot = key - t * page_size;
-        const int page = min(max(table[t], 0), last_page);
-        return head_base + static_cast<size_t>(page) * page_stride + static_cast<size_t>(slot) * slot_stride;
+        return {table[t], key - t * page_size};
+    }
+    __device__ size_t offset(Ref r) const
+    {
+        const int page = min(max(r.page, 0), last_page);
+        return head_base + static_cast<size_t>(page) * page_stride + static_cast<size_t>(r.slot) * slot_stride;
     }
 };
 
@@ -120,19 +133,32 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParam
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 
+    // Every lane reads a real row: a key past the chunk's end reads the
+    // chunk's last row instead (and gets weight 0 below), so the loads need
+    // no branch and the row lookups of the next iteration can be in flight
+    // while this one computes.
+    typename Rows::Ref ref[kDecUnroll];
+    auto lookup = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) ref[u] = row_of.ref(min(base + u * GROUPS + grp, ke - 1));
+    };
+    if (ks < ke) lookup(ks);
+
     for (int base = ks; base < ke; base += STEP) {
         u32x4 kr[kDecUnroll], vr[kDecUnroll];
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
-            const int key = base + u * GROUPS + grp;
-            u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-            if (key < ke) {
-                const size_t row = row_of(key);
-                kx = *reinterpret_cast<const u32x4 *>(Kg + row);
-                vx = *reinterpret_cast<const u32x4 *>(Vg + row);
-            }
-            kr[u] = kx;
-            vr[u] = vx;
+            const size_t row = row_of.offset(ref[u]);
+            kr[u] = *reinterpret_cast<const u32x4 *>(Kg + row);
+            vr[u] = *reinterpret_cast<const u32x4 *>(Vg + row);
+        }
+        lookup(base + STEP);
+        if (base + STEP > ke) {
+            // the stand-in rows of keys past the end: zero values, so that a
+            // weight of 0 contributes exactly 0 whatever the row holds
+#pragma unroll
+            for (int u = 0; u < kDecUnroll; ++u)
+                if (base + u * GROUPS + grp >= ke) vr[u] = u32x4{0, 0, 0, 0};
         }
         float t[kDecUnroll];
         float mx = -INFINITY;
