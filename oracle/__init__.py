@@ -16,6 +16,10 @@ and, for the backward with dL/dO = dO, the chain rule through that definition:
     dV = P^T dO, dP = dO V^T, D = rowsum(P * dP), dS = P * (dP - D),
     dQ = scale * dS K, dK = scale * dS^T Q
 
+decode over a paged cache (the dense attention over each sequence's keys,
+gathered through a block table), and the FP8 variant (Q and K rounded to
+E4M3 -- nearest even, saturating at 448 -- before the first product).
+
 All functions pinned by tests/test_oracle_pins.py (brute force at 50 digits,
 torch float64 SDPA, closed forms and invariants); no function here is
 "parity unpinned".
@@ -78,6 +82,13 @@ class Oracle:
         lib.fa_oracle_paged_decode.argtypes = [_dp, _dp, _dp, _i32p, _i32p, _dp, _dp, _i64, _i64, _i64, _i64,
                                                _i64, _i64, ctypes.c_int, ctypes.c_double]
         lib.fa_oracle_paged_decode.restype = ctypes.c_int
+        lib.fa_oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        lib.fa_oracle_e4m3_to_f64.restype = ctypes.c_double
+        lib.fa_oracle_quantize_e4m3.argtypes = [_dp, ctypes.POINTER(ctypes.c_uint8), _i64]
+        lib.fa_oracle_quantize_e4m3.restype = ctypes.c_int
+        lib.fa_oracle_attention_fp8qk.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, _i64,
+                                                  ctypes.c_int, ctypes.c_double]
+        lib.fa_oracle_attention_fp8qk.restype = ctypes.c_int
         lib.fa_oracle_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -206,6 +217,53 @@ class Oracle:
             raise ValueError(f"oracle rejected the call (rc={rc})")
         return o, lse
 
+    # -- FP8 (E4M3) Q and K -------------------------------------------------
+    def quantize_e4m3(self, x, dtype=None) -> np.ndarray:
+        """E4M3 codes (uint8) of x: round to nearest even, saturate beyond 448."""
+        x = self._as_f64(x, dtype)
+        codes = np.empty(x.shape, dtype=np.uint8)
+        rc = self.lib.fa_oracle_quantize_e4m3(_ptr(x), _ptr(codes, ctypes.c_uint8), x.size)
+        if rc:
+            raise ValueError("quantize failed")
+        return codes
+
+    def e4m3_to_f64(self, codes) -> np.ndarray:
+        """Exact values of E4M3 codes."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        table = np.array([self.lib.fa_oracle_e4m3_to_f64(c) for c in range(256)], dtype=np.float64)
+        return table[codes]
+
+    def attention_fp8qk(self, q, k, v, *, causal: bool, scale: float, dtype=None, k_codes: bool = False):
+        """Attention with Q and K quantised to E4M3 first: O [B,H,Nq,d], LSE [B,H,Nq].
+
+        q, v are as for attention(); k is the same, or E4M3 codes (uint8) when
+        k_codes is set (a cache already held in FP8)."""
+        q, v = self._as_f64(q, dtype), self._as_f64(v, dtype)
+        k = self.e4m3_to_f64(k) if k_codes else self._as_f64(k, dtype)
+        squeeze = q.ndim == 2
+        if squeeze:
+            q, k, v = q[None, None], k[None, None], v[None, None]
+        B, H, Nq, d = q.shape
+        Nkv = k.shape[2]
+        if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
+            raise ValueError("shape mismatch")
+        o = np.empty((B, H, Nq, d), dtype=np.float64)
+        lse = np.empty((B, H, Nq), dtype=np.float64)
+        rc = self.lib.fa_oracle_attention_fp8qk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nkv, d,
+                                                int(bool(causal)), float(scale))
+        if rc:
+            raise ValueError(f"oracle rejected the call (rc={rc})")
+        if squeeze:
+            return o[0, 0], lse[0, 0]
+        return o, lse
+
+    def attention_fp8qk_rows(self, q, k, v, rows, *, causal: bool, scale: float, dtype=None, k_codes: bool = False):
+        """Selected query rows of one head for the FP8 variant: Q and K are
+        quantised (through the same codec), then attention_rows runs."""
+        q8 = self.e4m3_to_f64(self.quantize_e4m3(q, dtype))
+        k8 = self.e4m3_to_f64(k if k_codes else self.quantize_e4m3(k, dtype))
+        return self.attention_rows(q8, k8, self._as_f64(v, dtype), rows, causal=causal, scale=scale)
+
     def threads(self) -> int:
         return int(self.lib.fa_oracle_threads())
 
@@ -243,6 +301,22 @@ def attention_bwd_sampled(q, k, v, dout, qrows, kcols, *, causal, scale, dtype=N
 def paged_decode(q, k_pages, v_pages, block_table, seq_lens, *, scale, layout="hnd", dtype=None):
     return default().paged_decode(q, k_pages, v_pages, block_table, seq_lens, scale=scale, layout=layout,
                                   dtype=dtype)
+
+
+def quantize_e4m3(x, dtype=None):
+    return default().quantize_e4m3(x, dtype)
+
+
+def e4m3_to_f64(codes):
+    return default().e4m3_to_f64(codes)
+
+
+def attention_fp8qk(q, k, v, *, causal, scale, dtype=None, k_codes=False):
+    return default().attention_fp8qk(q, k, v, causal=causal, scale=scale, dtype=dtype, k_codes=k_codes)
+
+
+def attention_fp8qk_rows(q, k, v, rows, *, causal, scale, dtype=None, k_codes=False):
+    return default().attention_fp8qk_rows(q, k, v, rows, causal=causal, scale=scale, dtype=dtype, k_codes=k_codes)
 
 
 def threads() -> int:

@@ -502,3 +502,102 @@ int fa_oracle_paged_decode(const double *q, const double *kpool, const double *v
     }
     return 0;
 }
+
+/*
+ * FP8 (OCP E4M3, "e4m3fn") for the forward with Q and K in 8 bits.
+ *
+ * The variant quantises Q and K to FP8 for the first product while V, P and
+ * O keep their 16-bit type, with fp32 accumulation ("FlashAttention 1-2-3:
+ * The IO-Aware Revolution in LLM Inference", section "FlashAttention-3: FP8,
+ * Async Warp Overlap, and Hopper-Specific Optimizations"; FP32 accumulation
+ * of the exponentials in "The Math Behind the Online Softmax Trick").  The
+ * pages name no scaling factor, so the reading taken is a direct cast of each
+ * value: round to the nearest E4M3 value, ties to even, and saturate
+ * magnitudes above the largest finite value 448 (infinities included) to
+ * +-448; NaN stays NaN.  The attention is then the ordinary definition above
+ * evaluated on the quantised Q and K.
+ *
+ * E4M3: sign bit, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent field
+ * 0 holds the subnormals m * 2^-9; field e in 1..15 holds (8 + m) * 2^(e - 10);
+ * field 15 with mantissa 7 is NaN, and there is no infinity.
+ */
+double fa_oracle_e4m3_to_f64(uint8_t code)
+{
+    const int e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);
+    return (code & 0x80) ? -v : v;
+}
+
+uint8_t fa_oracle_f64_to_e4m3(double x)
+{
+    if (isnan(x))
+        return 0x7F;
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs(x);
+    if (a >= 448.0)
+        return sign | 0x7E;            /* the largest finite value; beyond it saturate */
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal grid, step 2^-9; a result of 8 is the smallest normal (code 0x08) */
+        const double q = nearbyint(ldexp(a, 9));
+        return sign | (uint8_t)q;
+    }
+    int E;
+    frexp(a, &E);                      /* a = f * 2^E, f in [0.5, 1): a in [2^(E-1), 2^E) */
+    int e = E - 1;                     /* a in [2^e, 2^(e+1)), e >= -6 */
+    double q = nearbyint(ldexp(a, 3 - e)); /* multiples of the step 2^(e-3): q in [8, 16] */
+    if (q == 16.0) {
+        q = 8.0;
+        e += 1;
+    }
+    /* a < 448 = 14 * 2^5 keeps the result at or below 448 (field 15, mantissa 6) */
+    return sign | (uint8_t)(((e + 7) << 3) | (int)(q - 8.0));
+}
+
+int fa_oracle_quantize_e4m3(const double *x, uint8_t *codes, int64_t n)
+{
+    if (n < 0)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        codes[i] = fa_oracle_f64_to_e4m3(x[i]);
+    return 0;
+}
+
+/* The values the quantised tensor holds: x rounded to E4M3 and read back. */
+static void quantised_copy(const double *x, double *y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = fa_oracle_e4m3_to_f64(fa_oracle_f64_to_e4m3(x[i]));
+}
+
+/*
+ * Attention with Q and K quantised to E4M3 (see above) and V as given:
+ * quantise, then the three passes of standard attention in fp64.  Shapes and
+ * return codes as fa_oracle_attention.
+ */
+int fa_oracle_attention_fp8qk(const double *q, const double *k, const double *v, double *o, double *lse,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, int causal,
+                              double scale)
+{
+    if (B < 0 || H < 0 || check_shape(Nq, Nkv, d, causal))
+        return -1;
+    const int64_t nq = B * H * Nq * d, nk = B * H * Nkv * d;
+    double *q8 = (double *)malloc((size_t)(nq > 0 ? nq : 1) * sizeof(double));
+    double *k8 = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+    if (!q8 || !k8) {
+        free(q8);
+        free(k8);
+        return -2;
+    }
+    quantised_copy(q, q8, nq);
+    quantised_copy(k, k8, nk);
+    const int rc = fa_oracle_attention(q8, k8, v, o, lse, B, H, Nq, Nkv, d, causal, scale);
+    free(q8);
+    free(k8);
+    return rc;
+}

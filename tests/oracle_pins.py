@@ -521,10 +521,121 @@ def pin_paged_empty_and_single(orc):
             assert np.all(o[1, h] == 0.0) and lse[1, h] == -np.inf, (o[1, h], lse[1, h])
 
 
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) Q and K
+
+def _torch_e4m3_codes(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_decode_torch(orc):
+    # every one of the 256 codes decodes to torch's float8_e4m3fn value
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ours = orc.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def pin_e4m3_quantize_torch(orc):
+    # in range, the rounding is torch's float8_e4m3fn cast (nearest, ties to
+    # even): all finite binary16 values and a spread of bfloat16 values
+    h = np.arange(65536, dtype=np.uint16)
+    x = h.view(np.float16).astype(np.float64)
+    keep = np.isfinite(x) & (np.abs(x) <= 448)
+    ours = orc.quantize_e4m3(h[keep], "f16")
+    ref = _torch_e4m3_codes(x[keep])
+    assert np.array_equal(ours, ref), int(np.sum(ours != ref))
+    rng = _rng(111)
+    b = rng.integers(0, 65536, 20000).astype(np.uint16)
+    xb = orc.widen(b, "bf16")
+    kb = np.isfinite(xb) & (np.abs(xb) <= 448)
+    assert np.array_equal(orc.quantize_e4m3(b[kb], "bf16"), _torch_e4m3_codes(xb[kb]))
+
+
+def pin_e4m3_grid_and_saturation(orc):
+    # closed forms: every E4M3 value is a fixed point, the midpoint of two
+    # neighbours goes to the one with the even code, magnitudes above 448
+    # (infinity included) saturate, NaN stays NaN
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = orc.e4m3_to_f64(codes)
+    assert np.array_equal(orc.quantize_e4m3(vals), codes)
+    pos = np.sort(orc.e4m3_to_f64(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = orc.quantize_e4m3(mids)
+    lo = np.arange(0, 0x7E, dtype=np.uint8)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8))
+    big = np.array([448.0, 449.0, 463.9, 464.0, 470.0, 479.0, 1e6, np.inf, -500.0, -np.inf])
+    assert np.array_equal(orc.quantize_e4m3(big), np.array([0x7E] * 8 + [0xFE] * 2, dtype=np.uint8))
+    assert (orc.quantize_e4m3(np.array([np.nan])) & 0x7F) == 0x7F
+
+
+def pin_fp8_attention_identity(orc):
+    # Q and K already on the E4M3 grid: quantising changes nothing, so the
+    # FP8 attention equals the ordinary attention exactly
+    rng = _rng(113)
+    codes = rng.integers(0, 0x7E, (2, 2, 2, 24, 16)).astype(np.uint8) | (rng.integers(0, 2, (2, 2, 2, 24, 16)) << 7).astype(np.uint8)
+    codes = np.where((codes >> 3) & 15 > 9, codes & 0x87, codes)  # keep magnitudes moderate
+    q, k = orc.e4m3_to_f64(codes[0]), orc.e4m3_to_f64(codes[1])
+    v = rng.standard_normal((2, 2, 24, 16))
+    for causal in (False, True):
+        o8, l8 = orc.attention_fp8qk(q, k, v, causal=causal, scale=0.3)
+        o, l = orc.attention(q, k, v, causal=causal, scale=0.3)
+        assert np.array_equal(o8, o) and np.array_equal(l8, l)
+
+
+def pin_fp8_attention_torch(orc):
+    # off the grid: torch float64 attention on torch-quantised Q and K
+    import torch
+    rng = _rng(117)
+    B, H, Nq, Nkv, d = 1, 2, 20, 33, 32
+    q = (rng.standard_normal((B, H, Nq, d)) * 1.5).astype(np.float16)
+    k = (rng.standard_normal((B, H, Nkv, d)) * 1.5).astype(np.float16)
+    v = rng.standard_normal((B, H, Nkv, d)).astype(np.float16)
+    for causal in (False, True):
+        o8, l8 = orc.attention_fp8qk(q.view(np.uint16), k.view(np.uint16), v.view(np.uint16), causal=causal,
+                                     scale=0.2, dtype="f16")
+        tq = torch.from_numpy(q.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64)
+        tk = torch.from_numpy(k.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64)
+        tv = torch.from_numpy(v.astype(np.float64))
+        s = 0.2 * tq @ tk.transpose(-1, -2)
+        if causal:
+            i = torch.arange(Nq)[:, None]
+            j = torch.arange(Nkv)[None, :]
+            s = s.masked_fill(j > i + (Nkv - Nq), float("-inf"))
+        _close(o8, (torch.softmax(s, -1) @ tv).numpy(), tol=1e-12, what="fp8 attention O")
+        _close(l8, torch.logsumexp(s, -1).numpy(), tol=1e-12, what="fp8 attention LSE")
+        # and the quantisation matters: the 16-bit attention differs
+        o16, _ = orc.attention(q.view(np.uint16), k.view(np.uint16), v.view(np.uint16), causal=causal, scale=0.2,
+                               dtype="f16")
+        assert np.max(np.abs(o16 - o8)) > 1e-4
+
+
+def pin_fp8_rows_match_full(orc):
+    rng = _rng(119)
+    q = (rng.standard_normal((40, 16)) * 2).astype(np.float16).view(np.uint16)
+    k = (rng.standard_normal((50, 16)) * 2).astype(np.float16).view(np.uint16)
+    v = rng.standard_normal((50, 16)).astype(np.float16).view(np.uint16)
+    rows = np.array([0, 7, 39], dtype=np.int64)
+    o, lse = orc.attention_fp8qk(q, k, v, causal=True, scale=0.25, dtype="f16")
+    ro, rl = orc.attention_fp8qk_rows(q, k, v, rows, causal=True, scale=0.25, dtype="f16")
+    _close(ro, o[rows], tol=1e-12, what="fp8 rows O")
+    _close(rl, lse[rows], tol=1e-12, what="fp8 rows LSE")
+    kc = orc.quantize_e4m3(k, "f16")
+    ko, kl = orc.attention_fp8qk(q, kc, v, causal=True, scale=0.25, dtype="f16", k_codes=True)
+    assert np.array_equal(ko, o) and np.array_equal(kl, lse)
+
+
 PINS = [
     pin_widen_f16, pin_widen_bf16, pin_decimal_bruteforce, pin_torch_sdpa, pin_two_key_worked,
     pin_constant_v, pin_q_zero, pin_causal_row0, pin_dominant_score, pin_single_key, pin_bounds,
     pin_linearity, pin_permutation, pin_shift_invariance, pin_merge_identity, pin_rows_match_full,
     pin_head_independence, pin_widened_inputs, pin_bwd_torch_autograd, pin_bwd_finite_difference,
     pin_bwd_invariants, pin_bwd_sampled_matches_full, pin_paged_matches_dense, pin_paged_empty_and_single,
+    pin_e4m3_decode_torch, pin_e4m3_quantize_torch, pin_e4m3_grid_and_saturation, pin_fp8_attention_identity,
+    pin_fp8_attention_torch, pin_fp8_rows_match_full,
 ]

@@ -49,6 +49,12 @@ MUTANTS = [
     ("paged values gathered from the key pool", "memcpy(vd + j * d, vpool + row * d",
      "memcpy(vd + j * d, kpool + row * d"),
     ("paged empty sequence LSE", "lse[b * H + h] = -INFINITY;", "lse[b * H + h] = 0.0;"),
+    ("e4m3 rounds half away from zero", "double q = nearbyint(ldexp(a, 3 - e));", "double q = round(ldexp(a, 3 - e));"),
+    ("e4m3 subnormal step off by one", "const double q = nearbyint(ldexp(a, 9));",
+     "const double q = nearbyint(ldexp(a, 8)) * 2;"),
+    ("e4m3 exponent bias 8", "v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);"),
+    ("e4m3 saturates from 480 on", "if (a >= 448.0)", "if (a >= 480.0)"),
+    ("fp8 attention leaves K unquantised", "quantised_copy(k, k8, nk);", "memcpy(k8, k, (size_t)nk * sizeof(double));"),
 ]
 
 
