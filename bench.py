@@ -14,15 +14,17 @@ bytes (K and V once, q, o and lse).  rank 0 prints one JSON line.
 
 Separately from the step, the backward (fa_bwd: dQ, dK, dV from O and LSE,
 with dO from the seeded generator) is timed on the prefill workload and
-reported in its own "backward" object, and decode over a paged cache
-(fa_decode_paged: the decode cache scattered into a shuffled pool of 16-key
-pages) in a "paged_decode" object; neither is part of `value`.
+reported in its own "backward" object, the FP8 variant (fa_fwd_fp8: Q and K
+rounded to E4M3 for the first product) on the prefill workload in an
+"fp8_forward" object, and decode over a paged cache (fa_decode_paged: the
+decode cache scattered into a shuffled pool of 16-key pages) in a
+"paged_decode" object; none of them is part of `value`.
 
 The CPU baseline is the fp64 oracle (plain standard attention that
 materialises the score matrix) timed on a sample of the prefill heads on the
 host's cores; it is a reference point, not the target.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-paged]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-fp8] [--no-paged]
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ if ROOT not in sys.path:
 
 METRIC = "fwd attention TFLOP/s & % MFMA peak, N=8192 d=128 causal; decode HBM GB/s"
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak (published)
+PEAK_MFMA_F8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak (published)
 PREFILL = "prefill_8k_d128"
 DECODE = "decode_32k_d128"
@@ -174,6 +177,57 @@ def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
     }
 
 
+def time_fp8_forward(fa, fi, w, q, k, v, stream, warmup, steps):
+    """fa_fwd_fp8 on workload w: K rounded to E4M3 once (timed on its own), then
+    the forward with Q rounded in the kernel, each call bracketed by HIP events."""
+    import statistics
+
+    import torch
+    sp = stream.cuda_stream
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=k.device)
+    code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=q.device)
+
+    def quant():
+        fa.fa_quantize_e4m3(k, k8, k.numel(), code, sp)
+
+    def call():
+        fa.fa_fwd_fp8(q, k8, v, o, lse, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal, w.scale, code, sp)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    qms = timed(quant)
+    ms = timed(call)
+    mean = statistics.fmean(ms)
+    flops = metric_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
+    tflops = flops / (mean * 1e-3) / 1e12
+    # half the FLOPs (Q K^T) at the E4M3 rate, half (P V) at the 16-bit rate
+    mixed_peak = 1.0 / (0.5 / PEAK_MFMA_F8_TFLOPS + 0.5 / PEAK_MFMA_F16_TFLOPS)
+    return {
+        "workload": w.name,
+        "ms_mean": round(mean, 4),
+        "ms_min": round(min(ms), 4),
+        "flops": flops,
+        "TFLOP/s": round(tflops, 2),
+        "frac_of_mixed_peak": round(tflops / mixed_peak, 4),
+        "mixed_peak_TFLOP/s": round(mixed_peak, 1),
+        "quantize_k_ms": round(statistics.fmean(qms), 4),
+        "note": "Q K^T on the E4M3 MFMA (5.0 PFLOP/s peak), P V in 16 bits (2.5 PFLOP/s); K rounded to E4M3 once "
+                "before the timed calls (quantize_k_ms), Q inside the kernel",
+    }
+
+
 def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
     """fa_decode_paged on workload w: the dense decode cache k, v scattered into a
     shuffled page pool, each call bracketed by HIP events."""
@@ -241,6 +295,8 @@ def main():
                     help="skip the separate timing of the backward (fa_bwd) on the prefill workload")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the separate timing of decode over a paged cache (fa_decode_paged)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the separate timing of the FP8 Q/K forward (fa_fwd_fp8) on the prefill workload")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -378,6 +434,9 @@ def main():
     if run_prefill and not args.no_bwd:
         log("backward (fa_bwd) on the prefill workload")
         result["backward"] = time_backward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
+    if run_prefill and not args.no_fp8:
+        log("FP8 Q/K forward (fa_fwd_fp8) on the prefill workload")
+        result["fp8_forward"] = time_fp8_forward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
     if run_decode and not args.no_paged:
         log("decode over a paged cache (fa_decode_paged)")
         result["paged_decode"] = time_paged_decode(fa, fi, fi.WORKLOADS[PAGED], dq, dk, dv, stream, args.warmup,

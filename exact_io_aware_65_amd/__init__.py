@@ -26,9 +26,13 @@ from ._binding import (  # noqa: F401
     fa_decode_paged,
     fa_decode_workspace_size,
     fa_fwd,
+    fa_fwd_fp8,
     fa_last_error,
+    fa_quantize_e4m3,
     fa_status_str,
     fa_version,
     fwd,
+    fwd_fp8,
     library,
+    quantize_e4m3,
 )

@@ -5,11 +5,12 @@ kernels of libfa355.so.  PyTorch supplies device memory and the current
 stream.  The library must have been built (``python -m
 exact_io_aware_65_amd.build``); there is no fallback of any kind.
 
-Thin wrappers with the C names (``fa_fwd``, ``fa_decode``, ``fa_decode_paged``,
-``fa_bwd``, ...)
+Thin wrappers with the C names (``fa_fwd``, ``fa_fwd_fp8``, ``fa_decode``,
+``fa_decode_paged``, ``fa_bwd``, ...)
 take device pointers or tensors and raise :class:`FaError` on a non-OK
-status.  The convenience functions :func:`fwd`, :func:`decode`,
-:func:`decode_paged` and :func:`bwd` allocate the outputs.
+status.  The convenience functions :func:`fwd`, :func:`fwd_fp8`,
+:func:`quantize_e4m3`, :func:`decode`, :func:`decode_paged` and :func:`bwd`
+allocate the outputs.
 """
 from __future__ import annotations
 
@@ -52,6 +53,10 @@ def library() -> ctypes.CDLL:
         lib.fa_decode_workspace_size.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i, i, i, i]
         lib.fa_decode_num_splits.restype = i
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+        lib.fa_fwd_fp8.restype = i
+        lib.fa_quantize_e4m3.argtypes = [vp, vp, ctypes.c_size_t, i, vp]
+        lib.fa_quantize_e4m3.restype = i
         i32p = ctypes.POINTER(ctypes.c_int32)
         lib.fa_decode_paged.argtypes = [vp, vp, vp, i32p, i32p, vp, vp, i, i, i, i, i, i, i, i, f, i, i, vp,
                                         ctypes.c_size_t, vp]
@@ -88,6 +93,15 @@ def _check(status: int):
 def fa_fwd(q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, dtype, stream=None) -> None:
     _check(library().fa_fwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, H, Nq, Nkv, d,
                             int(bool(causal)), float(scale), int(dtype), _addr(stream)))
+
+
+def fa_fwd_fp8(q, k8, v, o, lse, B, H, Nq, Nkv, d, causal, scale, dtype, stream=None) -> None:
+    _check(library().fa_fwd_fp8(_addr(q), _addr(k8), _addr(v), _addr(o), _addr(lse), B, H, Nq, Nkv, d,
+                                int(bool(causal)), float(scale), int(dtype), _addr(stream)))
+
+
+def fa_quantize_e4m3(x, y, n, dtype, stream=None) -> None:
+    _check(library().fa_quantize_e4m3(_addr(x), _addr(y), int(n), int(dtype), _addr(stream)))
 
 
 def fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, dtype, num_splits, workspace, workspace_bytes,
@@ -189,6 +203,52 @@ def fwd(q, k, v, *, causal=False, scale=None, out_dtype=None, with_lse=True):
     o = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if with_lse else None
     fa_fwd(q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, code, _stream(q.device))
+    return o, lse
+
+
+def quantize_e4m3(x):
+    """E4M3 bytes (a uint8 tensor shaped like x) of a contiguous float16 / bfloat16 GPU tensor."""
+    import torch
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    fa_quantize_e4m3(x, y, x.numel(), _dtype_code(x), _stream(x.device))
+    return y
+
+
+def fwd_fp8(q, k, v, *, causal=False, scale=None, out_dtype=None, with_lse=True):
+    """fwd with Q and K rounded to E4M3 for the first product.
+
+    k is either 16-bit like q (rounded here by fa_quantize_e4m3) or already
+    E4M3: a uint8 or torch.float8_e4m3fn tensor [B, H, Nkv, d].  Returns (o, lse)."""
+    import torch
+    if k.dtype in (torch.float16, torch.bfloat16):
+        if k.dtype != q.dtype:
+            raise TypeError("a 16-bit k must have q's dtype")
+        _check_inputs(q, k, v)
+        k8 = quantize_e4m3(k)
+    elif k.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        _check_inputs(q, v, v)
+        if not k.is_cuda or not k.is_contiguous() or k.device != q.device:
+            raise ValueError("k must be a contiguous GPU tensor on q's device")
+        k8 = k
+    else:
+        raise TypeError(f"k must be float16, bfloat16, uint8 or float8_e4m3fn, got {k.dtype}")
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    code = _dtype_code(q)
+    odt = q.dtype
+    if out_dtype is not None and out_dtype != q.dtype:
+        if out_dtype != torch.float32:
+            raise TypeError("out_dtype must be None, q.dtype or torch.float32")
+        code |= FA_OUT_F32
+        odt = torch.float32
+    o = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if with_lse else None
+    fa_fwd_fp8(q, k8, v, o, lse, B, H, Nq, Nkv, d, causal, scale, code, _stream(q.device))
     return o, lse
 
 

@@ -20,7 +20,7 @@ LIBRARY = os.path.join(PKG, "libfa355.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_abi.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_abi.cpp"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",

@@ -80,7 +80,7 @@ constexpr unsigned __int128 kMaxElems = static_cast<unsigned __int128>(1) << 62;
 
 // Checks shared by fa_fwd and fa_decode once there is work to do.
 int check_tensors(const char *fn, const void *q, const void *k, const void *v, const void *o,
-                  const float *lse, int B, int H, int Nq, int Nkv, int d, bool out_f32)
+                  const float *lse, int B, int H, int Nq, int Nkv, int d, bool out_f32, int k_elt = 2)
 {
     if (!q || !k || !v || !o) return fail(FA_ERR_INVALID, "%s: q, k, v and o must be non-NULL", fn);
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16))
@@ -90,7 +90,7 @@ int check_tensors(const char *fn, const void *q, const void *k, const void *v, c
     const unsigned __int128 nq_el = bh * Nq * d, nkv_el = bh * Nkv * d;
     if (nq_el >= kMaxElems || nkv_el >= kMaxElems)
         return fail(FA_ERR_INVALID, "%s: tensor sizes exceed 2^62 elements", fn);
-    const Span in[3] = {span("q", q, nq_el * 2), span("k", k, nkv_el * 2), span("v", v, nkv_el * 2)};
+    const Span in[3] = {span("q", q, nq_el * 2), span("k", k, nkv_el * k_elt), span("v", v, nkv_el * 2)};
     const Span out_o = span("o", o, nq_el * (out_f32 ? 4 : 2));
     for (const Span &s : in)
         if (overlap(out_o, s)) return fail(FA_ERR_INVALID, "%s: o overlaps %s", fn, s.name);
@@ -147,6 +147,59 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
         std::fprintf(stderr, "fa355: fa_fwd B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x grid=%lld\n",
                      B, H, Nq, Nkv, d, causal != 0, dtype, blocks);
     const hipError_t err = fa355::launch_fwd(a, stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return FA_OK;
+}
+
+int fa_fwd_fp8(const void *q, const void *k8, const void *v, void *o, float *lse, int B, int H, int Nq, int Nkv,
+               int d, int causal, float scale, int dtype, hipStream_t stream)
+{
+    static const char *fn = "fa_fwd_fp8";
+    fa355::Elem elem;
+    bool out_f32;
+    int rc = parse_dtype(fn, dtype, &elem, &out_f32);
+    if (rc) return rc;
+    if ((rc = check_head_dim(fn, d))) return rc;
+    if (B < 0 || H < 0 || Nq < 0 || Nkv < 0)
+        return fail(FA_ERR_INVALID, "%s: negative size (B=%d H=%d Nq=%d Nkv=%d)", fn, B, H, Nq, Nkv);
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID, "%s: scale must be finite", fn);
+    if (B == 0 || H == 0 || Nq == 0) return FA_OK;  // empty output: nothing to do
+    if (Nkv == 0) return fail(FA_ERR_INVALID, "%s: Nkv=0: attention over no keys is undefined", fn);
+    if (causal && Nq > Nkv)
+        return fail(FA_ERR_INVALID, "%s: causal attention needs Nq <= Nkv (got %d > %d)", fn, Nq, Nkv);
+    if ((rc = check_tensors(fn, q, k8, v, o, lse, B, H, Nq, Nkv, d, out_f32, 1))) return rc;
+    if (static_cast<unsigned long long>(Nkv) * d * 2 > 0xffffffffULL ||
+        static_cast<unsigned long long>(Nq) * d * (out_f32 ? 4 : 2) > 0xffffffffULL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: one head of q, v or o exceeds 4 GiB", fn);
+    const int rows = fa355::fwd_rows_per_block(d);
+    const long long blocks = static_cast<long long>(B) * H * ((Nq + rows - 1) / rows);
+    if (blocks > 0x7fffffffLL)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+
+    fa355::FwdArgs a{q, k8, v, o, lse, B, H, Nq, Nkv, d, causal != 0, scale, elem, out_f32};
+    a.k_e4m3 = true;
+    if (log_enabled())
+        std::fprintf(stderr, "fa355: fa_fwd_fp8 B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x grid=%lld\n", B,
+                     H, Nq, Nkv, d, causal != 0, dtype, blocks);
+    const hipError_t err = fa355::launch_fwd(a, stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return FA_OK;
+}
+
+int fa_quantize_e4m3(const void *x, void *y, size_t n, int dtype, hipStream_t stream)
+{
+    static const char *fn = "fa_quantize_e4m3";
+    if (dtype != FA_F16 && dtype != FA_BF16)
+        return fail(FA_ERR_INVALID, "%s: dtype 0x%x is not FA_F16 or FA_BF16", fn, dtype);
+    if (n == 0) return FA_OK;
+    if (!x || !y || misaligned(x, 16) || misaligned(y, 16))
+        return fail(FA_ERR_INVALID, "%s: x and y must be non-NULL and 16-byte aligned", fn);
+    if (static_cast<unsigned __int128>(n) >= kMaxElems)
+        return fail(FA_ERR_INVALID, "%s: n exceeds 2^62 elements", fn);
+    if (overlap(span("x", x, static_cast<unsigned __int128>(n) * 2), span("y", y, n)))
+        return fail(FA_ERR_INVALID, "%s: y overlaps x", fn);
+    const hipError_t err = fa355::launch_quantize_e4m3(x, y, n, dtype == FA_F16 ? fa355::Elem::F16 : fa355::Elem::BF16,
+                                                       stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
     return FA_OK;
 }

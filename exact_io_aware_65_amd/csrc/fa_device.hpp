@@ -43,6 +43,28 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// FP8 operands: 32 E4M3 bytes per lane.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// D(32x32, fp32) += A(32x64) * B(64x32) on OCP E4M3 operands.  Lane l supplies
+// row (A) or column (B) l % 32 and 32 k-slots chosen by l / 32, byte j of its
+// 8 words being k-slot j of its half, the same way for A and B; D as for
+// mfma32.
+__device__ __forceinline__ f32x16 mfma32_e4m3(i32x8 a, i32x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// fp32 -> E4M3 (OCP): nearest, ties to even; magnitudes beyond the largest
+// finite value 448 (infinities included) saturate; NaN stays NaN.  Four
+// values into one word, the first in the low byte.
+__device__ __forceinline__ float sat448(float x) { return x != x ? x : __builtin_amdgcn_fmed3f(x, 448.f, -448.f); }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
+{
+    const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0u, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+}
+
 template <typename V> __device__ __forceinline__ V as(u32x4 x) { return __builtin_bit_cast(V, x); }
 
 // Round-to-nearest-even conversions of fp32 pairs to the storage type,

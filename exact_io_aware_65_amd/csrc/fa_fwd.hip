@@ -84,9 +84,16 @@ __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1)
 // cover 4 consecutive rows (starting at a multiple of 4) x 64 bytes, so the 4
 // rows must land in 4 distinct 64-byte bank segments.  For d = 64 two rows
 // share one 256-byte bank line, hence the extra shift by one row bit.
-template <int D> __device__ __forceinline__ int kswz(int row)
+//
+// K rows are 2d bytes (16-bit K) or d bytes (E4M3 K): 256, 128 or 64 bytes,
+// i.e. one, a half or a quarter of a 256-byte bank line.  The 16 rows read
+// together are 16 consecutive rows, so the row bits below the line take the
+// low bits of the bank-group index and the rest of the XOR spreads the rows
+// that share them.
+template <int ROWB> __device__ __forceinline__ int kswz(int row)
 {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    static_assert(ROWB == 256 || ROWB == 128 || ROWB == 64, "K rows of 256, 128 or 64 bytes");
+    return ROWB == 256 ? (row & 15) : ROWB == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 template <int D> __device__ __forceinline__ int vswz(int row)
 {
@@ -112,25 +119,37 @@ template <int L, int K> __device__ __forceinline__ void wait_loads(int n)
 constexpr int lcm2(int n) { return n % 2 ? 2 * n : n; }
 
 // NW waves of 32 query rows each (BM = 32 NW rows per workgroup) and a ring
-// of NS K/V stages.
-template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS>
+// of NS K/V stages.  KF8: Q and K enter the first product as E4M3 ("FlashAttention
+// 1-2-3 ...", section "FlashAttention-3": Q and K in FP8, V and O in 16 bits,
+// fp32 accumulation).  K then arrives already quantised (d bytes per row, half
+// the LDS bytes of the 16-bit tile), Q is quantised here as it is loaded, and
+// S^T = K Q^T runs on the 32x32x64 E4M3 MFMA; everything after the scores is
+// unchanged.
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p)
 {
     constexpr int BN = kBN, BM = 32 * NW, NT = 64 * NW;
-    constexpr int DC = D / 8;            // 16-byte chunks per row
-    constexpr int TILE = BN * DC;        // chunks per K (or V) tile
-    constexpr int LOADS = TILE / NT;     // direct loads per thread per tensor per tile
-    constexpr int ROWB = D * 2;          // bytes per row
-    constexpr int KS = D / 16;           // k-steps of the first product
-    constexpr int DT = D / 32;           // 32-dim blocks of the output
-    constexpr int U = lcm2(NS);          // steps per loop iteration (stage and score-set periods)
+    constexpr int DC = D / 8;               // 16-byte chunks per Q, V or O row
+    constexpr int TILE = BN * DC;           // chunks per V tile
+    constexpr int LOADS = TILE / NT;        // direct loads per thread per V tile
+    constexpr int ROWB = D * 2;             // bytes per Q, V or O row
+    constexpr int KROWB = KF8 ? D : 2 * D;  // bytes per K row
+    constexpr int KDC = KROWB / 16;         // chunks per K row
+    constexpr int KTILE = BN * KDC;         // chunks per K tile
+    constexpr int LOADS_K = KTILE / NT;     // direct loads per thread per K tile
+    constexpr int KS = KF8 ? D / 64 : D / 16;  // k-steps of the first product
+    constexpr int DT = D / 32;              // 32-dim blocks of the output
+    constexpr int U = lcm2(NS);             // steps per loop iteration (stage and score-set periods)
     static_assert(NS >= 2 && TILE % NT == 0 && LOADS >= 1 && LOADS <= 4, "tile must split evenly over the threads");
+    static_assert(KTILE % NT == 0 && LOADS_K >= 1 && LOADS_K <= (KROWB == 256 ? 4 : KROWB == 128 ? 2 : 1),
+                  "the K load offsets below assume these splits");
     static_assert(NS * TILE * 16 <= 65536, "stage offsets must fit the 16-bit LDS immediate");
     using V8 = typename Vec<T>::v8;
+    using QOp = typename std::conditional<KF8, i32x8, V8>::type;
 
-    __shared__ u32x4 sk[NS][TILE];  // K tiles [key][dim], chunk-permuted
-    __shared__ u32x4 sv[NS][TILE];  // V tiles [key][dim], chunk-permuted
+    __shared__ u32x4 sk[NS][KTILE];  // K tiles [key][dim], chunk-permuted
+    __shared__ u32x4 sv[NS][TILE];   // V tiles [key][dim], chunk-permuted
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
@@ -158,39 +177,57 @@ void fwd_kernel(FwdParams p)
     // which fills the ragged end of the last tile (those keys are masked) and
     // the query rows past Nq.
     const size_t q_head = static_cast<size_t>(bh) * p.Nq * ROWB;
-    const size_t kv_head = static_cast<size_t>(bh) * p.Nkv * ROWB;
+    const size_t k_head = static_cast<size_t>(bh) * p.Nkv * KROWB;
+    const size_t v_head = static_cast<size_t>(bh) * p.Nkv * ROWB;
     const auto rq = make_rsrc(static_cast<const char *>(p.q) + q_head, static_cast<uint32_t>(p.Nq) * ROWB);
-    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
-    const u32x4 rv = make_rsrc_words(static_cast<const char *>(p.v) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
+    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + k_head, static_cast<uint32_t>(p.Nkv) * KROWB);
+    const u32x4 rv = make_rsrc_words(static_cast<const char *>(p.v) + v_head, static_cast<uint32_t>(p.Nkv) * ROWB);
 
-    // Q operand, loaded once: lane (c, h) holds query wq0 + c, dims 16 s + 8 h .. + 7.
+    // Q operand, loaded once: lane (c, h) holds query wq0 + c, dims 16 s + 8 h .. + 7
+    // (16-bit), or dims 64 s + 32 h .. + 31 rounded to E4M3 (KF8).
     const int qrow = wq0 + c;
-    V8 qf[KS];
+    QOp qf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const u32x4 x = buffer_load16(rq, qrow * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.qsign;
-        qf[s] = as<V8>(x);
+        if constexpr (KF8) {
+            i32x8 w;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 x = buffer_load16(rq, qrow * ROWB + (64 * s + 32 * h + 8 * t) * 2, 0) ^ p.qsign;
+                w[2 * t] = static_cast<int>(e4m3x4(lo_f32<T>(x[0]), hi_f32<T>(x[0]), lo_f32<T>(x[1]), hi_f32<T>(x[1])));
+                w[2 * t + 1] = static_cast<int>(e4m3x4(lo_f32<T>(x[2]), hi_f32<T>(x[2]), lo_f32<T>(x[3]), hi_f32<T>(x[3])));
+            }
+            qf[s] = w;
+        } else {
+            const u32x4 x = buffer_load16(rq, qrow * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.qsign;
+            qf[s] = as<V8>(x);
+        }
     }
 
     // Direct loads: the wave's i-th load of a tensor fills LDS chunks
     // [(wave*LOADS + i)*64, +64) lane by lane; the lane fetches whichever
     // global chunk the permutation puts there.  Load i sits 1024 bytes after
     // load 0 both in memory and in LDS (the instruction offset), and only the
-    // K permutation changes with i, as an XOR on bits 6.. of the offset.
+    // K permutation changes with i, as an XOR on bits 6.. of the offset (the
+    // static_assert above keeps i within the range where that holds).
     uint32_t koff0, voff0;
+    {
+        const int pch = wave * LOADS_K * 64 + lane;
+        const int row = pch / KDC, col = pch % KDC;
+        koff0 = row * KROWB + ((col ^ kswz<KROWB>(row)) << 4);
+    }
     {
         const int pch = wave * LOADS * 64 + lane;
         const int row = pch / DC, col = pch % DC;
-        koff0 = row * ROWB + ((col ^ kswz<D>(row)) << 4);
         voff0 = row * ROWB + ((col ^ vswz<D>(row)) << 4);
     }
     auto issue_k = [&](auto st, int kb) {
-        const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
-        const u32x4 *dst = &sk[decltype(st)::value][wave * LOADS * 64];
+        const uint32_t tile = static_cast<uint32_t>(kb) * BN * KROWB;
+        const u32x4 *dst = &sk[decltype(st)::value][wave * LOADS_K * 64];
         dma_to_lds16<0>(rk, koff0, tile, dst);
-        if constexpr (LOADS > 1) dma_to_lds16<1024>(rk, koff0 ^ (1u << 6), tile, dst);
-        if constexpr (LOADS > 2) dma_to_lds16<2048>(rk, koff0 ^ (2u << 6), tile, dst);
-        if constexpr (LOADS > 3) dma_to_lds16<3072>(rk, koff0 ^ (3u << 6), tile, dst);
+        if constexpr (LOADS_K > 1) dma_to_lds16<1024>(rk, koff0 ^ (1u << 6), tile, dst);
+        if constexpr (LOADS_K > 2) dma_to_lds16<2048>(rk, koff0 ^ (2u << 6), tile, dst);
+        if constexpr (LOADS_K > 3) dma_to_lds16<3072>(rk, koff0 ^ (3u << 6), tile, dst);
     };
     auto issue_v = [&](auto st, int kb) {
         const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
@@ -207,19 +244,23 @@ void fwd_kernel(FwdParams p)
         int n = 0;
 #pragma unroll
         for (int i = j + 3 - NS; i <= j; ++i)
-            if (i >= 1 - NS) n += LOADS * ((i + NS - 1 < nkb) + (i + NS < nkb));
+            if (i >= 1 - NS) n += LOADS * (i + NS - 1 < nkb) + LOADS_K * (i + NS < nkb);
         return n;
     };
+    // LOADS is a multiple of LOADS_K, so every allowance is one too
+    constexpr int kMaxWait = (NS - 2) * (LOADS + LOADS_K) / LOADS_K;
 
     // LDS byte offsets of this lane's MFMA operands within a tile.
-    // K operand (kk, s): row 32 kk + swap23(c), logical chunk 2 s + h.  The
-    // permutation is an XOR on the chunk index, so step s is the step-0 offset
-    // with bits 5.. of the in-row byte offset XOR-ed by s; kk adds 32 rows,
-    // which leaves the permutation unchanged.
+    // K operand (kk, s): row 32 kk + swap23(c), logical chunk 2 s + h (16-bit)
+    // or the two chunks 4 s + 2 h and 4 s + 2 h + 1 (E4M3).  The permutation is
+    // an XOR on the chunk index and these chunk numbers are the step-0 chunk
+    // with disjoint higher bits set, so every operand is the step-0 offset
+    // XOR-ed by a constant; kk adds 32 rows, which leaves the permutation
+    // unchanged.
     uint32_t ka0;
     {
         const int krow = swap23(c);
-        ka0 = krow * ROWB + ((h ^ kswz<D>(krow)) << 4);
+        ka0 = krow * KROWB + (((KF8 ? 2 * h : h) ^ kswz<KROWB>(krow)) << 4);
     }
     // V^T operand (dt, kk, u, half): lane 16 g + 4 j + q addresses key
     // 32 kk + 16 u + 8 (g / 2) + j + 4 half and dims 32 dt + 16 (g % 2) + 4 q .. + 3,
@@ -254,8 +295,18 @@ void fwd_kernel(FwdParams p)
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ (s << 5)) + kk * 32 * ROWB);
-                sn[kk] = mfma32(as<V8>(x), qf[s], sn[kk]);
+                if constexpr (KF8) {
+                    const char *base = SK + kk * 32 * KROWB;
+                    const u32x4 x0 = *reinterpret_cast<const u32x4 *>(base + (ka0 ^ ((4 * s) << 4)));
+                    const u32x4 x1 = *reinterpret_cast<const u32x4 *>(base + (ka0 ^ ((4 * s + 1) << 4)));
+                    const i32x8 a = {static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]),
+                                     static_cast<int>(x0[3]), static_cast<int>(x1[0]), static_cast<int>(x1[1]),
+                                     static_cast<int>(x1[2]), static_cast<int>(x1[3])};
+                    sn[kk] = mfma32_e4m3(a, qf[s], sn[kk]);
+                } else {
+                    const u32x4 x = *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ (s << 5)) + kk * 32 * KROWB);
+                    sn[kk] = mfma32(as<V8>(x), qf[s], sn[kk]);
+                }
             }
     };
 
@@ -404,7 +455,7 @@ void fwd_kernel(FwdParams p)
             rowsum_p(pf);
             mx = rowmax(sn);
         }
-        wait_loads<LOADS, 2 * (NS - 2)>(allowance(j));
+        wait_loads<LOADS_K, kMaxWait>(allowance(j));
         __syncthreads();
     };
 
@@ -414,7 +465,7 @@ void fwd_kernel(FwdParams p)
     [&]<int... I>(std::integer_sequence<int, I...>) {
         ((I < nkb ? (issue_v(IC<I>{}, I), 0) : 0, I + 1 < nkb ? (issue_k(IC<I + 1>{}, I + 1), 0) : 0), ...);
     }(std::make_integer_sequence<int, NS - 1>{});
-    wait_loads<LOADS, 2 * (NS - 2)>(allowance(-1));
+    wait_loads<LOADS_K, kMaxWait>(allowance(-1));
     __syncthreads();
     if (nkw > 0) {
         scores(IC<0>{}, sa);
@@ -459,7 +510,7 @@ void fwd_kernel(FwdParams p)
 // loads already land within the step, and the chip is power-bound there.
 constexpr int kCUs = 256;
 
-template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS>
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8>
 hipError_t launch_shape(const FwdArgs &a, hipStream_t stream)
 {
     constexpr int BM = 32 * NW;
@@ -480,16 +531,27 @@ hipError_t launch_shape(const FwdArgs &a, hipStream_t stream)
     p.c = c < kMinC ? kMinC : c;
     p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_qt));
-    hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, OUT_F32, NW, NS>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, OUT_F32, NW, NS, KF8>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32, bool KF8>
+hipError_t launch_k(const FwdArgs &a, hipStream_t stream)
+{
+    // An E4M3 K tile of d = 64 (64 keys x 64 bytes) is one load per thread of
+    // a 4-wave workgroup: that shape only.
+    constexpr bool kWide = !(KF8 && D == 64);
+    const long long wide_blocks = static_cast<long long>(a.B) * a.H * ((a.Nq + 255) / 256);
+    if constexpr (kWide)
+        if (wide_blocks >= kCUs) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8>(a, stream);
+    return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2, KF8>(a, stream);
 }
 
 template <int D, typename T, bool CAUSAL, bool OUT_F32>
 hipError_t launch(const FwdArgs &a, hipStream_t stream)
 {
-    const long long wide_blocks = static_cast<long long>(a.B) * a.H * ((a.Nq + 255) / 256);
-    if (wide_blocks >= kCUs) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2>(a, stream);
-    return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2>(a, stream);
+    return a.k_e4m3 ? launch_k<D, T, CAUSAL, OUT_F32, true>(a, stream)
+                    : launch_k<D, T, CAUSAL, OUT_F32, false>(a, stream);
 }
 
 template <int D, typename T>

@@ -21,6 +21,7 @@ struct FwdArgs {
     float scale;
     Elem elem;
     bool out_f32;
+    bool k_e4m3 = false;  // k holds E4M3 bytes [B][H][Nkv][d]; q is quantised on the fly
 };
 
 struct DecodeArgs {
@@ -62,6 +63,8 @@ int fwd_rows_per_block(int d);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t stream);
+// x: n 16-bit values of type elem; y: n E4M3 bytes.  x 16-byte, y 8-byte aligned.
+hipError_t launch_quantize_e4m3(const void *x, void *y, std::size_t n, Elem elem, hipStream_t stream);
 
 // Workspace bytes of the backward: two fp32 values per query row.
 inline std::size_t bwd_workspace_bytes(int B, int H, int Nq)

@@ -82,7 +82,7 @@ extern "C" {
 /* HIP's opaque stream handle (identical to the typedef in hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define FA355_VERSION 3
+#define FA355_VERSION 4
 
 /* Element type of q, k, v (and of o unless FA_OUT_F32 is set). */
 enum fa_dtype {
@@ -110,6 +110,33 @@ enum fa_status {
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int H, int Nq, int Nkv, int d, int causal, float scale, int dtype,
            hipStream_t stream);
+
+/*
+ * Forward with Q and K in FP8 for the first product: FlashAttention-3's FP8
+ * mode ("FlashAttention 1-2-3 ...", section "FlashAttention-3: FP8, Async Warp
+ * Overlap, and Hopper-Specific Optimizations": Q and K quantised to FP8, V and
+ * O kept in 16 bits, fp32 accumulation).  The format is OCP E4M3 ("e4m3fn":
+ * bias 7, largest finite value 448, no infinity).  With no scaling factor on
+ * the pages, a value is quantised on its own: nearest E4M3 value, ties to
+ * even, magnitudes beyond 448 (infinities included) saturated to +-448.
+ *
+ *   O = softmax(scale * e4m3(q) k8^T [causal]) v,   LSE as for fa_fwd
+ *
+ * q, v, o, lse: as for fa_fwd (dtype names the type of q and v, and of o unless
+ * FA_OUT_F32).  k8: E4M3 bytes [B][H][Nkv][d] -- a cache already held in FP8,
+ * or the output of fa_quantize_e4m3 on a 16-bit K.  q is quantised inside the
+ * kernel as it is loaded.  Alignment, overlap and error rules as for fa_fwd.
+ */
+int fa_fwd_fp8(const void *q, const void *k8, const void *v, void *o, float *lse,
+               int B, int H, int Nq, int Nkv, int d, int causal, float scale, int dtype,
+               hipStream_t stream);
+
+/*
+ * Quantise n values of type dtype (FA_F16 or FA_BF16, no flags) at x to E4M3
+ * bytes at y, with the rounding fa_fwd_fp8 applies to q.  x and y are device
+ * memory, 16-byte aligned, not overlapping.  n = 0 is a no-op.
+ */
+int fa_quantize_e4m3(const void *x, void *y, size_t n, int dtype, hipStream_t stream);
 
 /*
  * Decode: one query per (b, h) against Nkv cached keys and values, all visible

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_num_splits", "fa_decode_paged",
-        "fa_decode_workspace_size", "fa_fwd", "fa_last_error", "fa_status_str", "fa_version"])
+        "fa_decode_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_last_error", "fa_status_str", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_version() == 3
+    assert fa.fa_version() == 4
     assert [fa.fa_status_str(s) for s in range(5)] == [
         "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP"]
     assert fa.fa_status_str(99) == "FA_ERR_UNKNOWN"
@@ -90,6 +90,46 @@ def test_fwd_rejects(kw, status, needle):
     got, msg = fwd(**kw)
     assert got == status, (got, msg)
     assert needle in msg, msg
+
+
+def fwd8(q=A, k=B_, v=C, o=O, lse=L, B=1, H=2, Nq=64, Nkv=64, d=128, causal=0, scale=0.125, dtype=fa.FA_F16):
+    return status_of(fa.fa_fwd_fp8, q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(k=None), fa.FA_ERR_INVALID, "non-NULL"),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED, "d=32"),
+    (dict(dtype=4), fa.FA_ERR_INVALID, "dtype"),
+    (dict(causal=1, Nq=65, Nkv=64), fa.FA_ERR_INVALID, "Nq <= Nkv"),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID, "finite"),
+    (dict(Nkv=0), fa.FA_ERR_INVALID, "no keys"),
+    (dict(k=B_ + 8), fa.FA_ERR_INVALID, "aligned"),
+    # k8 holds one byte per element: its last 16 of 2*64*128 bytes
+    (dict(o=B_ + 2 * 64 * 128 - 16), fa.FA_ERR_INVALID, "o overlaps k"),
+    (dict(lse=C + 64), fa.FA_ERR_INVALID, "lse overlaps v"),
+])
+def test_fwd_fp8_rejects(kw, status, needle):
+    got, msg = fwd8(**kw)
+    assert got == status, (got, msg)
+    assert needle in msg, msg
+
+
+def test_fwd_fp8_empty_is_noop():
+    assert fwd8(Nq=0, q=None, k=None, v=None, o=None, lse=None)[0] == fa.FA_OK
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((A, B_, 100, 3), fa.FA_ERR_INVALID, "dtype"),
+    ((A, B_, 100, fa.FA_F16 | fa.FA_OUT_F32), fa.FA_ERR_INVALID, "dtype"),
+    ((None, B_, 100, fa.FA_F16), fa.FA_ERR_INVALID, "non-NULL"),
+    ((A, B_ + 8, 100, fa.FA_F16), fa.FA_ERR_INVALID, "aligned"),
+    ((A, A + 192, 100, fa.FA_BF16), fa.FA_ERR_INVALID, "overlaps"),
+])
+def test_quantize_rejects(args, status, needle):
+    got, msg = status_of(fa.fa_quantize_e4m3, *args, None)
+    assert got == status, (got, msg)
+    assert needle in msg, msg
+    assert status_of(fa.fa_quantize_e4m3, None, None, 0, fa.FA_F16, None)[0] == fa.FA_OK
 
 
 def test_fwd_empty_is_noop():

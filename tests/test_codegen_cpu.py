@@ -43,7 +43,7 @@ def test_permlane_swap_uses_both_results(tmp_path):
 def test_no_packed_fp32_arithmetic(tmp_path):
     # packed fp32 add/mul/fma are kept out of the kernels
     asm = tmp_path / "k.s"
-    for src in ("fa_fwd.hip", "fa_decode.hip"):
+    for src in ("fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fp8.hip"):
         subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-I", os.path.join(ROOT, "include"),
                         "-I", CSRC, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-x", "hip",
                         "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", str(asm)],
@@ -73,7 +73,7 @@ def kernel_metadata(src, tmp_path):
 ONE_WAVE_PER_SIMD = ("bwd_dkdv_kernelILi128",)
 
 
-@pytest.mark.parametrize("src", ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip"])
+@pytest.mark.parametrize("src", ["fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fp8.hip"])
 def test_kernels_do_not_spill(src, tmp_path):
     kernels = kernel_metadata(src, tmp_path)
     assert kernels, f"no kernels found in {src}"
