@@ -82,8 +82,11 @@ def kernel_source_digest(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from rocprofv3 counters, if they were taken on the current kernel sources."""
+def measured_traffic(kernel, key=None):
+    """HBM bytes per launch from rocprofv3 counters, if they were taken on the current kernel sources.
+
+    kernel names the source group whose digest must match ("prefill" or
+    "decode"); key the record entry (default: that group's own launch)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.loads(f.read().split("```json", 1)[1].split("```", 1)[0])
@@ -91,7 +94,7 @@ def measured_traffic(kernel):
         return None
     if rec.get(f"{kernel}_digest") != kernel_source_digest(kernel):
         return None
-    return rec.get(f"{kernel}_bytes")
+    return rec.get(f"{key or kernel}_bytes")
 
 
 def calibrate_copy():
@@ -223,6 +226,7 @@ def time_fp8_forward(fa, fi, w, q, k, v, stream, warmup, steps):
         "frac_of_mixed_peak": round(tflops / mixed_peak, 4),
         "mixed_peak_TFLOP/s": round(mixed_peak, 1),
         "quantize_k_ms": round(statistics.fmean(qms), 4),
+        "traffic": measured_traffic("prefill", "fp8"),
         "note": "Q K^T on the E4M3 MFMA (5.0 PFLOP/s peak), P V in 16 bits (2.5 PFLOP/s); K rounded to E4M3 once "
                 "before the timed calls (quantize_k_ms), Q inside the kernel",
     }
@@ -275,6 +279,7 @@ def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
         "algorithmic_bytes": nbytes_alg,
         "GB/s": round(gbs, 1),
         "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "traffic": measured_traffic("decode", "paged"),
         "note": "the dense decode cache scattered into a shuffled pool of 16-key pages; bytes are K and V "
                 "once, q, o, lse, the block table and the lengths",
     }
