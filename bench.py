@@ -25,6 +25,7 @@ materialises the score matrix) timed on a sample of the prefill heads on the
 host's cores; it is a reference point, not the target.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-fp8] [--no-paged]
+    python bench.py --sweep [--steps K] [--warmup W]   # fused vs unfused over sequence length
 """
 from __future__ import annotations
 
@@ -232,6 +233,133 @@ def time_fp8_forward(fa, fi, w, q, k, v, stream, warmup, steps):
     }
 
 
+# ---------------------------------------------------------------------------
+# the unfused baseline and the speed-vs-length sweep
+
+def unfused_attention(q, k, v, causal, scale, mask=None):
+    """Standard attention with every intermediate in device memory ("FlashAttention",
+    section "The problem: the n x n score matrix"): S = (scale q) k^T in q's type,
+    masked, P = softmax(S) in q's type, O = P v -- three kernels and two n x n
+    tensors per head, the shape of PyTorch's math path.  A comparison point
+    only, built from torch's library GEMMs and softmax; mask, if given, is the
+    [Nq, Nkv] boolean of hidden keys."""
+    import torch
+    s = torch.matmul(q * scale, k.transpose(-1, -2).contiguous())
+    if causal:
+        if mask is None:
+            mask = causal_mask(q.shape[-2], k.shape[-2], q.device)
+        s.masked_fill_(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    return torch.matmul(p, v)
+
+
+def causal_mask(n_q, n_k, device):
+    """Keys hidden from each query row: j > i + (n_k - n_q)."""
+    import torch
+    return torch.ones(n_q, n_k, dtype=torch.bool, device=device).triu_(n_k - n_q + 1)
+
+
+def unfused_decode(q, k, v, scale):
+    """One query per head against the cache, unfused: s = K (scale q) in q's type
+    ([B, H, N, 1] in memory), p = softmax(s), o = p^T V."""
+    import torch
+    s = torch.matmul(k, (q * scale).unsqueeze(-1))
+    p = torch.softmax(s, dim=-2)
+    return torch.matmul(p.transpose(-1, -2).contiguous(), v).squeeze(-2)
+
+
+def _event_ms(fn, stream, warmup, steps):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return statistics.fmean(a.elapsed_time(b) for a, b in evs)
+
+
+SWEEP_PREFILL = (512, 1024, 2048, 4096, 8192, 16384, 32768)
+SWEEP_DECODE = (1024, 4096, 16384, 32768)
+
+
+def run_sweep(warmup, steps):
+    """fa_fwd against the unfused baseline over sequence lengths (B=1, H=32, d=128,
+    causal, fp16 -- the pages' benchmark shape), and fa_decode against unfused
+    decode over cache lengths (B=16, H=32, d=128).  Each length also reports the
+    largest |O_fused - O_unfused| and the device memory each path needs beyond
+    its inputs and outputs."""
+    import torch
+
+    import exact_io_aware_65_amd as fa
+    import fa_inputs as fi
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    out = {"prefill": [], "decode": []}
+    base = fi.WORKLOADS[PREFILL]
+    for n in SWEEP_PREFILL:
+        w = base.with_(name=f"sweep_prefill_{n}", Nq=n, Nkv=n)
+        x = fi.make_inputs(w)
+        q, k, v = (fi.bits_to_torch(x[t], w.dtype).to(dev) for t in "qkv")
+        x = None
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, n), dtype=torch.float32, device=dev)
+        mask = causal_mask(n, n, dev)
+        torch.cuda.synchronize()
+        fused = _event_ms(lambda: fa.fa_fwd(q, k, v, o, lse, w.B, w.H, n, n, w.d, True, w.scale, fa.FA_F16, sp),
+                          stream, warmup, steps)
+        base_mem = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        ou = unfused_attention(q, k, v, True, w.scale, mask)
+        torch.cuda.synchronize()
+        extra = torch.cuda.max_memory_allocated(dev) - base_mem - ou.numel() * ou.element_size()
+        diff = float((ou.float() - o.float()).abs().max())
+        ou = None
+        unf = _event_ms(lambda: unfused_attention(q, k, v, True, w.scale, mask), stream, warmup, steps)
+        flops = metric_flops(w.B, w.H, n, n, w.d, True)
+        out["prefill"].append({
+            "N": n, "fused_ms": round(fused, 4), "unfused_ms": round(unf, 4), "speedup": round(unf / fused, 2),
+            "fused_TFLOP/s": round(flops / (fused * 1e-3) / 1e12, 1),
+            "unfused_TFLOP/s": round(flops / (unf * 1e-3) / 1e12, 1),
+            "unfused_extra_bytes": int(extra), "fused_extra_bytes": 0, "max_abs_diff_O": diff})
+        print(f"[sweep] prefill N={n}: fused {fused:.3f} ms, unfused {unf:.3f} ms, x{unf / fused:.2f}",
+              file=sys.stderr, flush=True)
+        q = k = v = o = lse = mask = None
+        torch.cuda.empty_cache()
+    dbase = fi.WORKLOADS[DECODE]
+    for n in SWEEP_DECODE:
+        w = dbase.with_(name=f"sweep_decode_{n}", Nkv=n)
+        x = fi.make_inputs(w)
+        q = fi.bits_to_torch(x["q"][:, :, 0], w.dtype).to(dev)
+        k, v = (fi.bits_to_torch(x[t], w.dtype).to(dev) for t in "kv")
+        x = None
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        nbytes = fa.fa_decode_workspace_size(w.B, w.H, n, w.d, 0)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        fused = _event_ms(lambda: fa.fa_decode(q, k, v, o, lse, w.B, w.H, n, w.d, w.scale, fa.FA_F16, 0, ws, nbytes, sp),
+                          stream, warmup, steps)
+        ou = unfused_decode(q, k, v, w.scale)
+        torch.cuda.synchronize()
+        diff = float((ou.float() - o.float()).abs().max())
+        unf = _event_ms(lambda: unfused_decode(q, k, v, w.scale), stream, warmup, steps)
+        nb = algorithmic_bytes(w.B, w.H, 1, n, w.d)
+        out["decode"].append({
+            "Nkv": n, "fused_ms": round(fused, 4), "unfused_ms": round(unf, 4), "speedup": round(unf / fused, 2),
+            "fused_GB/s": round(nb / (fused * 1e-3) / 1e9, 1), "unfused_GB/s": round(nb / (unf * 1e-3) / 1e9, 1),
+            "fused_workspace_bytes": nbytes, "max_abs_diff_O": diff})
+        print(f"[sweep] decode Nkv={n}: fused {fused:.3f} ms, unfused {unf:.3f} ms, x{unf / fused:.2f}",
+              file=sys.stderr, flush=True)
+        q = k = v = o = lse = ws = None
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
     """fa_decode_paged on workload w: the dense decode cache k, v scattered into a
     shuffled page pool, each call bracketed by HIP events."""
@@ -300,11 +428,20 @@ def main():
                     help="skip the separate timing of the backward (fa_bwd) on the prefill workload")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the separate timing of decode over a paged cache (fa_decode_paged)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the speed-vs-length sweep of the fused kernels against the unfused baseline")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the separate timing of the FP8 Q/K forward (fa_fwd_fp8) on the prefill workload")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.sweep:
+        if args.gpus != 1:
+            sys.exit("bench.py --sweep measures one GPU only")
+        res = run_sweep(max(1, args.warmup), max(1, args.steps))
+        print(json.dumps({"metric": "fused vs unfused attention time over sequence length", "unit": "ms",
+                          "higher_is_better": False, "dtype": "f16", "data": "synthetic", "sweep": res}), flush=True)
         return
     if args.gpus != 1:
         if int(os.environ.get("RANK", "0")) == 0:
