@@ -102,22 +102,32 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key blocks of 128 (4 waves x 32 keys), query tiles of 64 (two
-// 32-query sub-tiles) through a two-stage LDS ring.
+// dK, dV: key blocks of 128 (4 waves x 32 keys), query tiles through a
+// two-stage LDS ring.  Two waves per SIMD, so that one wave's softmax runs
+// beside the other's MFMAs: K and the dK, dV accumulators stay in registers,
+// and for d = 128 V moves to LDS (read as the forward reads K) and the query
+// tiles shrink to 32 rows, which keeps a workgroup's LDS within half a CU's.
 
 template <int D, typename T, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p)
 {
-    constexpr int NW = 4, BK = 32 * NW, BQ = 64, NT = 64 * NW;
+    constexpr bool VLDS = D == 128;  // V operand from LDS rather than registers
+    constexpr int NW = 4, BK = 32 * NW, BQ = VLDS ? 32 : 64, NQQ = BQ / 32, NT = 64 * NW;
     constexpr int DC = D / 8, TILE = BQ * DC, LOADS = TILE / NT, ROWB = 2 * D, KS = D / 16, DT = D / 32;
-    static_assert(TILE % NT == 0, "tile must split evenly over the threads");
+    static_assert(TILE % NT == 0 && (BK * DC) % NT == 0, "tiles must split evenly over the threads");
     using V8 = typename Vec<T>::v8;
 
     __shared__ u32x4 sq[2][TILE];   // Q tiles [query][dim], dswz-permuted
     __shared__ u32x4 sdo[2][TILE];  // dO tiles [query][dim], dswz-permuted
-    __shared__ float sl2[2][BQ];    // base-2 LSE of the tile's queries
-    __shared__ float sdd[2][BQ];    // D of the tile's queries
+    // base-2 LSE and D of the tile's queries; wave 0 fills them with one
+    // 64-lane dword load each, so each stage holds 64 entries (with BQ = 32
+    // the second half is the next tile's, unused)
+    constexpr int LQ = BQ < 64 ? 64 : BQ;
+    static_assert(LQ == 64, "one wave-wide dword load per stage");
+    __shared__ float sl2[2][LQ];
+    __shared__ float sdd[2][LQ];
+    __shared__ u32x4 sv[VLDS ? BK * DC : 1];  // the block's V [key][dim], kswz-permuted
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,17 +153,30 @@ void bwd_dkdv_kernel(BwdParams p)
 
     // K and V as B operands of S = Q K^T and dP = dO V^T: lane (c, h) holds key
     // kw0 + c, dims 16 s + 8 h .. + 7 (zeros past Nkv).  K carries the sign of
-    // the scale.
-    V8 kf[KS], vf[KS];
+    // the scale.  With VLDS the block's V goes to LDS instead, each chunk
+    // permuted by kswz of its row; the lane then reads row 32 wave + c, logical
+    // chunk 2 s + h, conflict-free as the forward's K reads.
+    V8 kf[KS], vf[VLDS ? 1 : KS];
+    uint32_t va0 = 0;
     {
         const auto rk = make_rsrc(static_cast<const char *>(p.k) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
         const auto rv = make_rsrc(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             kf[s] = as<V8>(buffer_load16(rk, key * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.sign);
-            vf[s] = as<V8>(buffer_load16(rv, key * ROWB + (16 * s + 8 * h) * 2, 0));
+            if constexpr (!VLDS) vf[s] = as<V8>(buffer_load16(rv, key * ROWB + (16 * s + 8 * h) * 2, 0));
+        }
+        if constexpr (VLDS) {
+#pragma unroll
+            for (int i = 0; i < BK * DC / NT; ++i) {
+                const int ch = i * NT + tid, row = ch / DC, col = ch % DC;
+                sv[row * DC + (col ^ kswz<D>(row))] = buffer_load16(rv, (k0 + row) * ROWB + col * 16, 0);
+            }
+            const int vrow = 32 * wave + c;
+            va0 = vrow * ROWB + ((h ^ kswz<D>(vrow)) << 4);
         }
     }
+    const char *SV = reinterpret_cast<const char *>(sv);
 
     auto ld_off = [&](int i) {
         const int pch = (wave * LOADS + i) * 64 + lane;
@@ -211,7 +234,12 @@ void bwd_dkdv_kernel(BwdParams p)
         for (int ks = 0; ks < KS; ++ks) {
             const uint32_t a = (ra0 ^ (ks << 5)) + qq * 32 * ROWB;
             s = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SQ + a)), kf[ks], s);
-            dp = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SDO + a)), vf[ks], dp);
+            V8 vb;
+            if constexpr (VLDS)
+                vb = as<V8>(*reinterpret_cast<const u32x4 *>(SV + (va0 ^ (ks << 5))));
+            else
+                vb = vf[ks];
+            dp = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SDO + a)), vb, dp);
         }
         // this lane's queries: element e <-> query 8 h + e (e < 8), 16 + 8 h + e - 8
         const f32x4 *l2v = reinterpret_cast<const f32x4 *>(&sl2[st][32 * qq + 8 * h]);
@@ -261,7 +289,7 @@ void bwd_dkdv_kernel(BwdParams p)
         __syncthreads();  // tile t visible to every wave; tile t - 1's stage free
         if (t + 1 < nqt) issue(st ^ 1, t + 1);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
+        for (int qq = 0; qq < NQQ; ++qq) {
             const int qs0 = t * BQ + 32 * qq;
             // some (query, key) pair of the sub-tile is visible to this wave
             if (qs0 < p.Nq && (!CAUSAL || qs0 + 31 >= wfirst)) subtile(st, t, qq);
