@@ -416,8 +416,8 @@ def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--num-splits", type=int, default=0, help="decode split count (0 = library choice)")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
@@ -571,7 +571,9 @@ def main():
                    "ms_p50": round(pct(dec_ms, 0.5), 4), "ms_p90": round(pct(dec_ms, 0.9), 4),
                    "GB/s": round(gbs, 1), "algorithmic_bytes": d_bytes, "workspace_bytes": ws_bytes},
         "gpu": {"name": props.name, "cus": props.multi_processor_count,
-                "arch": getattr(props, "gcnArchName", "")},
+                "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip},
+        "sources": {"prefill_digest": kernel_source_digest("prefill"),
+                    "decode_digest": kernel_source_digest("decode")},
     }
     if run_prefill and not args.no_bwd:
         log("backward (fa_bwd) on the prefill workload")

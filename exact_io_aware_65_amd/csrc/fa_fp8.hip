@@ -24,9 +24,10 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_e4m3_kernel(const void
     const u32x4 *src = static_cast<const u32x4 *>(x);
     u32x2 *dst = static_cast<u32x2 *>(y);
     for (size_t i = static_cast<size_t>(blockIdx.x) * kQuantThreads + threadIdx.x; i < n8; i += stride) {
-        const u32x4 w = src[i];
-        dst[i] = u32x2{e4m3x4(lo_f32<T>(w[0]), hi_f32<T>(w[0]), lo_f32<T>(w[1]), hi_f32<T>(w[1])),
-                       e4m3x4(lo_f32<T>(w[2]), hi_f32<T>(w[2]), lo_f32<T>(w[3]), hi_f32<T>(w[3]))};
+        const u32x4 w = __builtin_nontemporal_load(src + i);  // each byte moves once
+        __builtin_nontemporal_store(u32x2{e4m3x4(lo_f32<T>(w[0]), hi_f32<T>(w[0]), lo_f32<T>(w[1]), hi_f32<T>(w[1])),
+                                          e4m3x4(lo_f32<T>(w[2]), hi_f32<T>(w[2]), lo_f32<T>(w[3]), hi_f32<T>(w[3]))},
+                                    dst + i);
     }
     // the last n % 8 elements, one per thread of the first workgroup
     const size_t tail = n8 * 8 + threadIdx.x;

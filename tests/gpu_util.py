@@ -46,10 +46,16 @@ def max_err(got, ref):
     return float(diff[worst]), tuple(int(i) for i in worst)
 
 
+def mean_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    return float(np.mean(np.abs(got - np.asarray(ref, dtype=np.float64)))) if got.size else 0.0
+
+
 def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what):
     eo, wo = max_err(o_gpu, o_ref)
     el, wl = max_err(lse_gpu, lse_ref)
-    say(f"{what}: err_O={eo:.3e} at {wo}, err_LSE={el:.3e} at {wl}")
+    say(f"{what}: err_O={eo:.3e} at {wo} (mean {mean_err(o_gpu, o_ref):.2e}), "
+        f"err_LSE={el:.3e} at {wl} (mean {mean_err(lse_gpu, lse_ref):.2e})")
     assert eo <= TOL_O[dtype], f"{what}: O error {eo:.3e} at {wo} exceeds {TOL_O[dtype]}"
     assert el <= TOL_LSE, f"{what}: LSE error {el:.3e} at {wl} exceeds {TOL_LSE}"
     return eo, el
