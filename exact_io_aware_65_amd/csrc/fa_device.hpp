@@ -1,5 +1,6 @@
 // Device-side building blocks for gfx950 (CDNA4, wave64): vector types, the
-// 32x32x16 MFMA, 16-bit conversions and cross-lane exchanges.
+// 32x32x16 (16-bit) and 32x32x64 (E4M3) MFMAs, conversions, buffer loads and
+// direct-to-LDS copies, and cross-lane exchanges.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -114,30 +115,12 @@ template <> __device__ __forceinline__ float dot2<__bf16>(uint32_t a, uint32_t b
                                            __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane i's bytes land at lds_base + 16 * i.  lds_base must be wave-uniform.
-// Completion is tracked by vmcnt, like any vector load.
-__device__ __forceinline__ void global_to_lds16(const void *gptr, void *lds_base)
-{
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-
 // Buffer resource over [base, base + bytes) (raw, stride 0).  Buffer
 // accesses are range-checked against `bytes`: reads past the end return 0
 // and touch no memory.  Limited to 2^32 - 1 bytes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Buffer -> LDS copy of 16 bytes per lane from byte offset voff + soff (soff
-// wave-uniform); lane i's bytes land at lds_base + 16 * i.  Out-of-range
-// lanes write zeros.
-__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                                void *lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voff, soff,
-                                             0, 0);
 }
 
 // Buffer resource as four scalar words: base address, stride 0, byte range
@@ -194,8 +177,6 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // output lane i, element j (16-bit) is element i % 4 of the 8 bytes addressed
