@@ -14,7 +14,8 @@ bytes (K and V once, q, o and lse).  rank 0 prints one JSON line.
 
 Separately from the step, the backward (fa_bwd: dQ, dK, dV from O and LSE,
 with dO from the seeded generator) is timed on the prefill workload and
-reported in its own "backward" object, the FP8 variant (fa_fwd_fp8: Q and K
+reported in its own "backward" object, the other two prefill workloads
+(2K d64 fp16 and 16K d128 bf16 causal) in "other_prefill", the FP8 variant (fa_fwd_fp8: Q and K
 rounded to E4M3 for the first product) on the prefill workload in an
 "fp8_forward" object, and decode over a paged cache (fa_decode_paged: the
 decode cache scattered into a shuffled pool of 16-key pages) in a
@@ -24,7 +25,7 @@ The CPU baseline is the fp64 oracle (plain standard attention that
 materialises the score matrix) timed on a sample of the prefill heads on the
 host's cores; it is a reference point, not the target.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-fp8] [--no-paged]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-other] [--no-fp8] [--no-paged]
     python bench.py --sweep [--steps K] [--warmup W]   # fused vs unfused over sequence length
 """
 from __future__ import annotations
@@ -360,6 +361,32 @@ def run_sweep(warmup, steps):
     return out
 
 
+OTHER_PREFILL = ("prefill_2k_d64", "prefill_16k_d128_bf16")
+
+
+def time_other_prefill(fa, fi, names, dev, stream, warmup, steps):
+    """fa_fwd on the other prefill workloads (reported beside the headline one, not part of `value`)."""
+    import torch
+    sp = stream.cuda_stream
+    res = []
+    for name in names:
+        w = fi.WORKLOADS[name]
+        x = fi.make_inputs(w)
+        q, k, v = (fi.bits_to_torch(x[t], w.dtype).to(dev) for t in "qkv")
+        x = None
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+        ms = _event_ms(lambda: fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal, w.scale, code, sp),
+                       stream, warmup, steps)
+        flops = metric_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
+        tf = flops / (ms * 1e-3) / 1e12
+        res.append({"workload": name, "B": w.B, "H": w.H, "N": w.Nq, "d": w.d, "dtype": w.dtype, "causal": w.causal,
+                    "ms_mean": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4)})
+        q = k = v = o = lse = None
+    return res
+
+
 def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
     """fa_decode_paged on workload w: the dense decode cache k, v scattered into a
     shuffled page pool, each call bracketed by HIP events."""
@@ -430,6 +457,8 @@ def main():
                     help="skip the separate timing of decode over a paged cache (fa_decode_paged)")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the speed-vs-length sweep of the fused kernels against the unfused baseline")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the timing of the other prefill workloads (2K d64, 16K d128 bf16)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the separate timing of the FP8 Q/K forward (fa_fwd_fp8) on the prefill workload")
     args = ap.parse_args()
@@ -578,6 +607,9 @@ def main():
     if run_prefill and not args.no_bwd:
         log("backward (fa_bwd) on the prefill workload")
         result["backward"] = time_backward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
+    if run_prefill and not args.no_other:
+        log("other prefill workloads (fa_fwd)")
+        result["other_prefill"] = time_other_prefill(fa, fi, OTHER_PREFILL, dev, stream, args.warmup, args.steps)
     if run_prefill and not args.no_fp8:
         log("FP8 Q/K forward (fa_fwd_fp8) on the prefill workload")
         result["fp8_forward"] = time_fp8_forward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
