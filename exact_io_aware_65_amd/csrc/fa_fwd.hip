@@ -125,11 +125,21 @@ constexpr int lcm2(int n) { return n % 2 ? 2 * n : n; }
 // the LDS bytes of the 16-bit tile), Q is quantised here as it is loaded, and
 // S^T = K Q^T runs on the 32x32x64 E4M3 MFMA; everything after the scores is
 // unchanged.
-template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8>
+//
+// KG = 2 (key groups) serves grids too small to fill the chip: the waves form
+// two groups that take the same query rows and alternate key tiles (group g
+// takes tiles g, g + 2, ...), each with its own LDS ring, and the two partial
+// results are merged exactly at the end through LDS, with the two-block merge
+// of "FlashAttention 1-2-3 ...", section "The Math Behind the Online Softmax
+// Trick".  That halves the serial chain of key tiles behind each query tile.
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8, int KG>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p)
 {
-    constexpr int BN = kBN, BM = 32 * NW, NT = 64 * NW;
+    static_assert(KG == 1 || KG == 2, "one or two key groups");
+    constexpr int WGW = NW / KG;            // waves per key group
+    constexpr int BN = kBN, BM = 32 * WGW;  // keys per tile, query rows per workgroup
+    constexpr int NT = 64 * WGW;            // threads of a key group (they fill its ring)
     constexpr int DC = D / 8;               // 16-byte chunks per Q, V or O row
     constexpr int TILE = BN * DC;           // chunks per V tile
     constexpr int LOADS = TILE / NT;        // direct loads per thread per V tile
@@ -148,11 +158,18 @@ void fwd_kernel(FwdParams p)
     using V8 = typename Vec<T>::v8;
     using QOp = typename std::conditional<KF8, i32x8, V8>::type;
 
-    __shared__ u32x4 sk[NS][KTILE];  // K tiles [key][dim], chunk-permuted
-    __shared__ u32x4 sv[NS][TILE];   // V tiles [key][dim], chunk-permuted
+    // K and V rings of each key group, [key][dim] tiles, chunk-permuted; with
+    // two key groups the same memory holds the partial results at the end.
+    __shared__ u32x4 lds_rings[KG * NS * (KTILE + TILE)];
+    u32x4(*const sk)[NS][KTILE] = reinterpret_cast<u32x4(*)[NS][KTILE]>(lds_rings);
+    u32x4(*const sv)[NS][TILE] = reinterpret_cast<u32x4(*)[NS][TILE]>(lds_rings + KG * NS * KTILE);
+    static_assert(KG == 1 || (WGW * (DT * 16 + 2) * 64 * 4 <= KG * NS * (KTILE + TILE) * 16),
+                  "the partial results of a key group fit the rings");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
+    const int grp = KG == 1 ? 0 : wave / WGW;                   // key group of the wave
+    const int rw = KG == 1 ? wave : wave % WGW;                 // its block of 32 query rows
     const int c = lane & 31, h = lane >> 5;
 
     // Heaviest causal tiles (last query rows) are dispatched first.  Consecutive
@@ -161,7 +178,7 @@ void fwd_kernel(FwdParams p)
     const int bh = blockIdx.x % p.n_bh;
     const int qt = p.n_qt - 1 - static_cast<int>(blockIdx.x / p.n_bh);
     const int q0 = qt * BM;
-    const int wq0 = q0 + 32 * wave;
+    const int wq0 = q0 + 32 * rw;
     const int off = p.Nkv - p.Nq;  // causal: row i sees keys j <= i + off
     int kend = p.Nkv;
     if constexpr (CAUSAL) kend = min(p.Nkv, min(q0 + BM, p.Nq) + off);
@@ -172,6 +189,11 @@ void fwd_kernel(FwdParams p)
         nkw = nkb;
         if constexpr (CAUSAL) nkw = min(nkb, (min(wq0 + 31, p.Nq - 1) + off) / BN + 1);
     }
+    // This group's share: local tile t is key tile KG t + grp.  Both groups run
+    // ntl steps (group 0's count), so every wave reaches every barrier.
+    const int ntl = (nkb + KG - 1) / KG;
+    const int nkb_g = (nkb - grp + KG - 1) / KG;  // tiles of the group's ring
+    const int nkw_g = (nkw - grp + KG - 1) / KG;  // of them, tiles this wave's rows can see
 
     // Per-head buffer descriptors: reads past a head's last row return zeros,
     // which fills the ragged end of the last tile (those keys are masked) and
@@ -212,26 +234,27 @@ void fwd_kernel(FwdParams p)
     // static_assert above keeps i within the range where that holds).
     uint32_t koff0, voff0;
     {
-        const int pch = wave * LOADS_K * 64 + lane;
+        const int pch = rw * LOADS_K * 64 + lane;
         const int row = pch / KDC, col = pch % KDC;
         koff0 = row * KROWB + ((col ^ kswz<KROWB>(row)) << 4);
     }
     {
-        const int pch = wave * LOADS * 64 + lane;
+        const int pch = rw * LOADS * 64 + lane;
         const int row = pch / DC, col = pch % DC;
         voff0 = row * ROWB + ((col ^ vswz<D>(row)) << 4);
     }
+    // kb: the group's local tile index
     auto issue_k = [&](auto st, int kb) {
-        const uint32_t tile = static_cast<uint32_t>(kb) * BN * KROWB;
-        const u32x4 *dst = &sk[decltype(st)::value][wave * LOADS_K * 64];
+        const uint32_t tile = static_cast<uint32_t>(KG * kb + grp) * BN * KROWB;
+        const u32x4 *dst = &sk[grp][decltype(st)::value][rw * LOADS_K * 64];
         dma_to_lds16<0>(rk, koff0, tile, dst);
         if constexpr (LOADS_K > 1) dma_to_lds16<1024>(rk, koff0 ^ (1u << 6), tile, dst);
         if constexpr (LOADS_K > 2) dma_to_lds16<2048>(rk, koff0 ^ (2u << 6), tile, dst);
         if constexpr (LOADS_K > 3) dma_to_lds16<3072>(rk, koff0 ^ (3u << 6), tile, dst);
     };
     auto issue_v = [&](auto st, int kb) {
-        const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
-        const u32x4 *dst = &sv[decltype(st)::value][wave * LOADS * 64];
+        const uint32_t tile = static_cast<uint32_t>(KG * kb + grp) * BN * ROWB;
+        const u32x4 *dst = &sv[grp][decltype(st)::value][rw * LOADS * 64];
         dma_to_lds16<0>(rv, voff0, tile, dst);
         if constexpr (LOADS > 1) dma_to_lds16<1024>(rv, voff0, tile, dst);
         if constexpr (LOADS > 2) dma_to_lds16<2048>(rv, voff0, tile, dst);
@@ -244,7 +267,7 @@ void fwd_kernel(FwdParams p)
         int n = 0;
 #pragma unroll
         for (int i = j + 3 - NS; i <= j; ++i)
-            if (i >= 1 - NS) n += LOADS * (i + NS - 1 < nkb) + LOADS_K * (i + NS < nkb);
+            if (i >= 1 - NS) n += LOADS * (i + NS - 1 < nkb_g) + LOADS_K * (i + NS < nkb_g);
         return n;
     };
     // LOADS is a multiple of LOADS_K, so every allowance is one too
@@ -286,7 +309,7 @@ void fwd_kernel(FwdParams p)
 
     // S^T = K Q^T for the K tile in stage st (two 32-key sub-tiles).
     auto scores = [&](auto st, f32x16 (&sn)[2]) {
-        const char *SK = reinterpret_cast<const char *>(sk[decltype(st)::value]);
+        const char *SK = reinterpret_cast<const char *>(sk[grp][decltype(st)::value]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -358,7 +381,11 @@ void fwd_kernel(FwdParams p)
     //    coarse for the log-sum-exp).
     constexpr bool kSumP = std::is_same<T, _Float16>::value;
     auto softmax = [&](f32x16 (&sc)[2], V8 (&pf)[2][2]) {
-        const float neg_m = -m_run;  // finite: every row sees key 0 in the first tile
+        // m_run is finite once a row has seen a key; with one key group every
+        // row sees key 0 in the first tile.  The second group's first tiles
+        // may hide every key from a row: then m_run is -inf and p must be 0.
+        float neg_m = -m_run;
+        if constexpr (KG > 1) neg_m = m_run == -INFINITY ? 0.f : neg_m;
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -414,7 +441,7 @@ void fwd_kernel(FwdParams p)
 
     // O^T += V^T P^T for the V tile in stage st (two transposed reads per operand).
     auto pv = [&](auto st, const V8 (&pf)[2][2]) {
-        const char *SV = reinterpret_cast<const char *>(sv[decltype(st)::value]);
+        const char *SV = reinterpret_cast<const char *>(sv[grp][decltype(st)::value]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -440,15 +467,15 @@ void fwd_kernel(FwdParams p)
     float mx = -INFINITY;
     auto step = [&](auto st, f32x16 (&sc)[2], f32x16 (&sn)[2], int j) {
         constexpr int S = decltype(st)::value % NS;
-        if (j + NS - 1 < nkb) issue_v(IC<(S + NS - 1) % NS>{}, j + NS - 1);
-        if (j + NS < nkb) issue_k(IC<S>{}, j + NS);
-        if (j < nkw) {
+        if (j + NS - 1 < nkb_g) issue_v(IC<(S + NS - 1) % NS>{}, j + NS - 1);
+        if (j + NS < nkb_g) issue_k(IC<S>{}, j + NS);
+        if (j < nkw_g) {
             rescale(mx);
             // phase 1: MFMAs of the next scores beside the softmax of the current ones
             scores(IC<(S + 1) % NS>{}, sn);
             softmax(sc, pf);
             pin(pf);  // P is formed here, not sunk past the mask branch
-            const int kv1 = (j + 1) * BN;
+            const int kv1 = (KG * (j + 1) + grp) * BN;
             if (needs_mask(kv1)) mask(sn, kv1);
             // phase 2: MFMAs of O += V P beside the row max of the next scores
             pv(IC<S>{}, pf);
@@ -461,28 +488,58 @@ void fwd_kernel(FwdParams p)
 
     // Prologue: K_0, then the requests of steps 1 - NS .. -1 (V_0 .. V_{NS-2},
     // K_1 .. K_{NS-1}); wait for K_0, V_0 and K_1, form S_0 and its row max.
-    issue_k(IC<0>{}, 0);
+    if (nkb_g > 0) issue_k(IC<0>{}, 0);
     [&]<int... I>(std::integer_sequence<int, I...>) {
-        ((I < nkb ? (issue_v(IC<I>{}, I), 0) : 0, I + 1 < nkb ? (issue_k(IC<I + 1>{}, I + 1), 0) : 0), ...);
+        ((I < nkb_g ? (issue_v(IC<I>{}, I), 0) : 0, I + 1 < nkb_g ? (issue_k(IC<I + 1>{}, I + 1), 0) : 0), ...);
     }(std::make_integer_sequence<int, NS - 1>{});
     wait_loads<LOADS_K, kMaxWait>(allowance(-1));
     __syncthreads();
-    if (nkw > 0) {
+    if (nkw_g > 0) {
         scores(IC<0>{}, sa);
-        if (needs_mask(0)) mask(sa, 0);
+        if (needs_mask(grp * BN)) mask(sa, grp * BN);
         mx = rowmax(sa);
     }
     __syncthreads();  // every wave is done with sk[0] before K_NS refills it
 
-    for (int j = 0; j < nkb; j += U) {
+    for (int j = 0; j < ntl; j += U) {
         [&]<int... I>(std::integer_sequence<int, I...>) {
-            ((j + I < nkb ? (I % 2 == 0 ? step(IC<I>{}, sa, sb, j + I) : step(IC<I>{}, sb, sa, j + I)), 0 : 0), ...);
+            ((j + I < ntl ? (I % 2 == 0 ? step(IC<I>{}, sa, sb, j + I) : step(IC<I>{}, sb, sa, j + I)), 0 : 0), ...);
         }(std::make_integer_sequence<int, U>{});
     }
 
     // Epilogue: O = acc / l, LSE = ln 2 * (m + log2 l).
-    const float l_tot = sum_with_other_half(l_run);
-    if (qrow < p.Nq) {
+    float l_tot = sum_with_other_half(l_run);
+    if constexpr (KG == 2) {
+        // Group 1 hands its partial result (accumulator, reference max, row
+        // sum; lane by lane, so the same lane of the partner wave holds the
+        // same query and dims) to group 0 through the rings' memory, which the
+        // last step's barrier has freed.  Group 0 merges:
+        //   M = max(m0, m1), O = (2^(m0-M) O0 + 2^(m1-M) O1) / (2^(m0-M) l0 + 2^(m1-M) l1).
+        float *xo = reinterpret_cast<float *>(lds_rings);  // [WGW][DT * 16][64]
+        float *xm = xo + WGW * DT * 16 * 64;              // [WGW][2][64]
+        if (grp == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) xo[((rw * DT + dt) * 16 + e) * 64 + lane] = oacc[dt][e];
+            xm[(rw * 2) * 64 + lane] = m_run;
+            xm[(rw * 2 + 1) * 64 + lane] = l_tot;
+        }
+        __syncthreads();
+        if (grp == 0) {
+            const float m1 = xm[(rw * 2) * 64 + lane], l1 = xm[(rw * 2 + 1) * 64 + lane];
+            const float mm = fmaxf(m_run, m1);  // finite: group 0 holds key 0
+            const float a0 = fast_exp2(m_run - mm), a1 = fast_exp2(m1 - mm);
+            l_tot = a0 * l_tot + a1 * l1;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    oacc[dt][e] = a0 * oacc[dt][e] + a1 * xo[((rw * DT + dt) * 16 + e) * 64 + lane];
+            m_run = mm;
+        }
+    }
+    if (qrow < p.Nq && grp == 0) {
         const float inv = 1.f / l_tot;
         const size_t orow = (static_cast<size_t>(bh) * p.Nq + qrow) * D;
 #pragma unroll
@@ -510,10 +567,10 @@ void fwd_kernel(FwdParams p)
 // loads already land within the step, and the chip is power-bound there.
 constexpr int kCUs = 256;
 
-template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8>
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8, int KG = 1>
 hipError_t launch_shape(const FwdArgs &a, hipStream_t stream)
 {
-    constexpr int BM = 32 * NW;
+    constexpr int BM = 32 * NW / KG;
     FwdParams p;
     p.q = a.q;
     p.k = a.k;
@@ -531,7 +588,7 @@ hipError_t launch_shape(const FwdArgs &a, hipStream_t stream)
     p.c = c < kMinC ? kMinC : c;
     p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_qt));
-    hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, OUT_F32, NW, NS, KF8>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, T, CAUSAL, OUT_F32, NW, NS, KF8, KG>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -547,6 +604,10 @@ hipError_t launch_k(const FwdArgs &a, hipStream_t stream)
     const long long wide_blocks = static_cast<long long>(a.B) * a.H * ((a.Nq + 255) / 256);
     if constexpr (kWide)
         if (wide_blocks >= kCUs) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8>(a, stream);
+    // Too few 128-row tiles to give every CU one: two key groups per tile
+    // halve the serial chain of key tiles (worth it from 4 key tiles on).
+    const long long tiles = static_cast<long long>(a.B) * a.H * ((a.Nq + 127) / 128);
+    if (tiles <= kCUs && a.Nkv > 3 * kBN) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8, 2>(a, stream);
     return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2, KF8>(a, stream);
 }
 
