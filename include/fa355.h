@@ -40,8 +40,9 @@
  *
  * Ownership.  Every pointer is device memory owned by the caller (for example
  * the storage of framework tensors).  The library allocates no device memory:
- * fa_fwd needs none, fa_decode uses only the caller's workspace.  No pointer
- * is retained after a call returns.
+ * fa_fwd, fa_fwd_fp8 and fa_quantize_e4m3 need none; fa_decode,
+ * fa_decode_paged and fa_bwd use only the caller's workspace.  No pointer is
+ * retained after a call returns.
  *
  * Execution.  Calls enqueue work on `stream` (NULL = the default stream) and
  * return without waiting; results are ready when the stream is synchronised.
