@@ -1,0 +1,94 @@
+"""API paths of the C ABI on the GPU: optional LSE, caller streams, shared workspaces.
+
+Each check compares one call path with another whose parity against the
+oracle is covered elsewhere, bit for bit: the kernels are deterministic, so a
+path that only changes plumbing must not change a single output bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_65_amd as fa
+import fa_inputs as fi
+from gpu_util import device, rand_bits, say, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(seed, B, H, Nq, Nkv, d, dtype="f16"):
+    rng = np.random.default_rng(seed)
+    return (upload(rand_bits(rng, (B, H, Nq, d), dtype), dtype), upload(rand_bits(rng, (B, H, Nkv, d), dtype), dtype),
+            upload(rand_bits(rng, (B, H, Nkv, d), dtype), dtype))
+
+
+def test_fwd_without_lse():
+    for case in ((1, 4, 300, 300, 128, True), (2, 2, 77, 500, 64, False), (1, 64, 512, 512, 128, True)):
+        B, H, Nq, Nkv, d, causal = case
+        q, k, v = _qkv(11, B, H, Nq, Nkv, d)
+        say(f"fa_fwd lse=NULL {case}")
+        o1, lse = fa.fwd(q, k, v, causal=causal)
+        o2, none = fa.fwd(q, k, v, causal=causal, with_lse=False)
+        o3, _ = fa.fwd_fp8(q, k, v, causal=causal)
+        o4, _ = fa.fwd_fp8(q, k, v, causal=causal, with_lse=False)
+        torch.cuda.synchronize()
+        assert none is None and torch.equal(o1, o2) and torch.equal(o3, o4)
+
+
+def test_decode_without_lse_and_shared_workspace():
+    B, H, d = 3, 4, 128
+    ws = torch.empty(fa.fa_decode_workspace_size(B, H, 4000, d, 0), dtype=torch.uint8, device=device())
+    for Nkv in (4000, 1000, 37):
+        q, k, v = _qkv(12 + Nkv, B, H, 1, Nkv, d)
+        q = q[:, :, 0].contiguous()
+        say(f"fa_decode lse=NULL, workspace sized for 4000 keys, Nkv={Nkv}")
+        o_ref, _ = fa.decode(q, k, v)
+        o = torch.empty_like(q)
+        need = fa.fa_decode_workspace_size(B, H, Nkv, d, 0)
+        assert need <= ws.numel()
+        fa.fa_decode(q, k, v, o, None, B, H, Nkv, d, 1 / np.sqrt(d), fa.FA_F16, 0, ws, ws.numel(),
+                     torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref)
+
+
+def test_paged_decode_without_lse():
+    B, H, d, N = 3, 2, 64, 500
+    plan = fi.paged_plan(13, B, N, 16, ragged=True)
+    rng = np.random.default_rng(13)
+    q = upload(rand_bits(rng, (B, H, d), "f16"), "f16")
+    kp = upload(fi.scatter_to_pages(rand_bits(rng, (B, H, N, d), "f16"), plan), "f16")
+    vp = upload(fi.scatter_to_pages(rand_bits(rng, (B, H, N, d), "f16"), plan), "f16")
+    table = torch.from_numpy(plan.block_table).to(device())
+    lens = torch.from_numpy(plan.seq_lens).to(device())
+    say("fa_decode_paged lse=NULL")
+    o_ref, _ = fa.decode_paged(q, kp, vp, table, lens, max_seq_len=N)
+    o = torch.empty_like(q)
+    nbytes = fa.fa_decode_workspace_size(B, H, N, d, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device())
+    fa.fa_decode_paged(q, kp, vp, table, lens, o, None, B, H, d, plan.num_pages, 16, plan.block_table.shape[1],
+                       fa.FA_PAGED_HND, N, 1 / np.sqrt(d), fa.FA_F16, 0, ws, nbytes,
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+
+
+def test_caller_stream():
+    # every entry point runs on the stream it is given (a second stream of
+    # default priority), ordered after work queued there before it
+    q, k, v = _qkv(14, 1, 4, 256, 256, 128)
+    ref_o, ref_lse = fa.fwd(q, k, v, causal=True)
+    ref_g = fa.bwd(q, k, v, ref_o, q, ref_lse, causal=True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    say("entry points on a caller stream")
+    with torch.cuda.stream(s):
+        q2, k2, v2 = q.clone(), k.clone(), v.clone()  # queued on s before the library calls
+        o, lse = fa.fwd(q2, k2, v2, causal=True)
+        g = fa.bwd(q2, k2, v2, o, q2, lse, causal=True)
+        od, _ = fa.decode(q2[:, :, :1].contiguous(), k2, v2)
+    s.synchronize()
+    od_ref, _ = fa.decode(q[:, :, :1].contiguous(), k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
+    assert all(torch.equal(a, b) for a, b in zip(g, ref_g))
+    assert torch.equal(od, od_ref)
