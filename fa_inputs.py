@@ -11,7 +11,9 @@ Generator recipe (one independent stream per tensor and head):
 with tensor 0 = Q, 1 = K, 2 = V and 4 = dO (the upstream gradient dL/dO for
 the backward, shaped like Q).  The "spike" workload additionally draws, per
 head, one key index j_h = default_rng([seed, 3, b, h]).integers(0, Nkv) and
-multiplies that K row by 20 before the cast.  Per-head seed sequences make the
+multiplies that K row by 20 before the cast; with spike_on="query" (the other
+reading of that workload) it draws a query index in [0, Nq) the same way and
+scales that Q row instead.  Per-head seed sequences make the
 generation order-free, so heads can be produced in parallel or one at a time
 (for sampled checks at full size) with identical bits.
 
@@ -57,6 +59,7 @@ class Workload:
     seed: int
     sigma_qk: float = 1.0  # standard deviation of Q and K entries
     spike: bool = False    # one K row per head multiplied by SPIKE_FACTOR
+    spike_on: str = "key"  # "query": the alternative reading, one Q row per head instead
     out_f32: bool = False  # O written as float32 instead of the input type
     decode: bool = False   # one query per (b, h) against the whole cache
     page_size: int = 0     # > 0: the decode cache is paged (see paged_plan)
@@ -127,8 +130,10 @@ def head_tensor(w: Workload, tensor: int, b: int, h: int) -> np.ndarray:
     x = normals(w.seed, tensor, b, h, n, w.d)
     if tensor in (Q, K) and w.sigma_qk != 1.0:
         x *= np.float32(w.sigma_qk)
-    if tensor == K and w.spike:
-        x[spike_index(w.seed, b, h, w.Nkv)] *= np.float32(SPIKE_FACTOR)
+    if w.spike_on not in ("key", "query"):
+        raise ValueError(f"spike_on must be 'key' or 'query', got {w.spike_on!r}")
+    if w.spike and tensor == (K if w.spike_on == "key" else Q):
+        x[spike_index(w.seed, b, h, n)] *= np.float32(SPIKE_FACTOR)
     return f32_to_bits(x, w.dtype)
 
 
@@ -157,9 +162,11 @@ def make_inputs(w: Workload) -> dict:
 
 
 def spike_indices(w: Workload) -> list:
+    """Per head (b-major), the spiked K row (or Q row when spike_on == "query")."""
     if not w.spike:
         return []
-    return [spike_index(w.seed, b, h, w.Nkv) for b in range(w.B) for h in range(w.H)]
+    n = w.Nkv if w.spike_on == "key" else w.Nq
+    return [spike_index(w.seed, b, h, n) for b in range(w.B) for h in range(w.H)]
 
 
 def head_inputs(w: Workload, b: int, h: int):

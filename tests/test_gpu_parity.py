@@ -286,3 +286,24 @@ def test_full_size_decode_sampled():
         o_ref, lse_ref = oracle.attention_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h], [0],
                                                causal=False, scale=w.scale, dtype=w.dtype)
         check(o_all[b, h], lse_all[b, h][None], o_ref, lse_ref, w.dtype, f"decode head {bh}")
+
+
+def test_spike_on_query_reading():
+    # the other reading of the spiked bf16 workload: one Q row per head x 20
+    # (scores of std ~20 in that row: a nearly one-hot softmax); full heads at
+    # a reduced length, the spiked rows and their neighbours sampled
+    w = fi.WORKLOADS["prefill_16k_d128_bf16"].with_(H=4, Nq=4096, Nkv=4096, spike_on="query")
+    say("generate spike-on-query workload")
+    x = fi.make_inputs(w)
+    say("fa_fwd spike-on-query")
+    o32, lse32 = fa.fwd(upload(x["q"], w.dtype), upload(x["k"], w.dtype), upload(x["v"], w.dtype), causal=w.causal,
+                        scale=w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o32).all() and torch.isfinite(lse32).all()
+    rng = np.random.default_rng(5)
+    for bh, i in enumerate(fi.spike_indices(w)):
+        rows = _sample_rows(w.Nq, rng, (i - 1, i, i + 1))
+        o_ref, lse_ref = oracle.attention_rows(x["q"][0, bh], x["k"][0, bh], x["v"][0, bh], rows, causal=w.causal,
+                                               scale=w.scale, dtype=w.dtype)
+        check(to_np(o32[0, bh])[rows], to_np(lse32[0, bh])[rows], o_ref, lse_ref, w.dtype,
+              f"spike-on-query head {bh} row {i}")

@@ -62,6 +62,22 @@ def test_spike_row():
         assert np.array_equal(k[0, h, other], fi.f32_to_bits(raw[other], "bf16"))
 
 
+def test_spike_on_query():
+    # the other reading of the spike workload: one Q row per head x 20, K untouched
+    w = fi.WORKLOADS["prefill_16k_d128_bf16"].with_(H=2, Nq=300, Nkv=320, spike_on="query")
+    q, k = fi.make_tensor(w, fi.Q), fi.make_tensor(w, fi.K)
+    idx = fi.spike_indices(w)
+    assert len(idx) == 2 and all(0 <= i < 300 for i in idx)
+    for h, i in enumerate(idx):
+        raw = fi.normals(w.seed, fi.Q, 0, h, 300, 128)
+        assert np.array_equal(q[0, h, i], fi.f32_to_bits(raw[i] * np.float32(20.0), "bf16"))
+        assert np.array_equal(q[0, h, (i + 1) % 300], fi.f32_to_bits(raw[(i + 1) % 300], "bf16"))
+    plain = fi.make_tensor(w.with_(spike=False), fi.K)
+    assert np.array_equal(k, plain)
+    with pytest.raises(ValueError):
+        fi.make_tensor(w.with_(spike_on="value"), fi.Q)
+
+
 def test_bits_roundtrip_torch():
     bits = np.array([0x3C00, 0xC000, 0x0001], dtype=np.uint16)
     t = fi.bits_to_torch(bits, "f16")
