@@ -6,10 +6,21 @@ chain-rule gradients evaluated in fp64 on the same 16-bit inputs.
 
 Tolerance: max |err| <= TOL_REL * max |ref| per gradient.  The backward rounds
 P and dS to the input type before the products that consume them (relative
-error u = 2^-11 for fp16, 2^-8 for bf16, at most half an ulp) and forms
-D = rowsum(dO * O) from the rounded forward output; a handful of such
-roundings per gradient entry bounds the error by a few u of the gradient's
-scale: TOL_REL = 10 u (fp16: 4.9e-3, bf16: 3.9e-2).
+error u = 2^-11 for fp16, 2^-8 for bf16, at most half an ulp); a handful of
+such roundings per gradient entry bounds the error by a few u of the
+gradient's scale: TOL_REL = 10 u (fp16: 4.9e-3, bf16: 3.9e-2).
+
+dQ carries one more term.  D = rowsum(dO * O) is formed from the forward
+output O in the input type, as the caller hands it over, so D_i is off by up
+to u * A_i with A_i = sum_c |dO_ic O_ic|.  That error enters every
+dS_ij = P_ij (dP_ij - D_i) of the row and reaches dQ_i = scale * sum_j dS_ij K_j
+as at most |scale| u A_i sum_j P_ij |K_jc|, which is not bounded by the scale
+of dQ itself: a key row much longer than the others (the spiked workload
+multiplies one K row by 20) multiplies it while the cancellation in
+dP - D keeps dQ small.  The dQ bound is therefore, element by element,
+TOL_REL * max |dQ_ref| + 2 |scale| u A_i sum_j P_ij |K_jc|, with O, P and A from
+the fp64 reference.  (dK = scale * dS^T Q sums the same D errors over queries
+weighted by P; it stays within TOL_REL on every workload here.)
 """
 import zlib
 
@@ -37,8 +48,27 @@ def run_fwd_bwd(q, k, v, do, causal, scale, dtype, out_f32=True):
     return tuple(to_np(x) for x in g)
 
 
-def check_grads(got, ref, dtype, what):
-    errs = []
+def d_term(q, k, v, dout, rows, causal, scale, dtype):
+    """2 |scale| u A_i sum_j P_ij |K_jc| for the query rows `rows` of one head ([len(rows), d], fp64).
+
+    q, k, v, dout are one head's 16-bit bit patterns ([N, d]); O, LSE come from
+    the fp64 reference, P and A are recomputed from them here in numpy."""
+    rows = np.asarray(rows, dtype=np.int64)
+    o, lse = oracle.attention_rows(q, k, v, rows, causal=causal, scale=scale, dtype=dtype)
+    qf = oracle.widen(q, dtype)[rows]
+    kf = oracle.widen(k, dtype)
+    dof = oracle.widen(dout, dtype)[rows]
+    Nq, Nkv = q.shape[0], k.shape[0]
+    s = scale * (qf @ kf.T)
+    if causal:
+        s = np.where(np.arange(Nkv)[None, :] <= rows[:, None] + (Nkv - Nq), s, -np.inf)
+    p = np.exp(s - lse[:, None])
+    a = np.sum(np.abs(dof * o), axis=1)
+    return 2.0 * abs(scale) * U[dtype] * a[:, None] * (p @ np.abs(kf))
+
+
+def check_grads(got, ref, dtype, what, dq_extra=None):
+    errs, bad = [], []
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         assert g.shape == r.shape, f"{what} {name}: shape {g.shape} vs {r.shape}"
         assert not np.isnan(g).any(), f"{what} {name}: NaN"
@@ -48,7 +78,17 @@ def check_grads(got, ref, dtype, what):
         mag = float(np.max(np.abs(r)))
         errs.append((name, err, mag))
         say(f"{what}: {name} max err {err:.3e} = {err / max(mag, 1e-300):.2e} of max|ref| {mag:.3e}")
-        assert err <= TOL_REL[dtype] * mag + 1e-30, f"{what} {name}: error {err:.3e} > {TOL_REL[dtype]:.1e} x {mag:.3e}"
+        bound = TOL_REL[dtype] * mag + 1e-30
+        if name == "dQ" and dq_extra is not None:
+            excess = np.abs(g - r) - (bound + dq_extra)
+            worst = np.unravel_index(int(np.argmax(excess)), excess.shape)
+            say(f"{what}: dQ with the D term: worst margin {float(excess[worst]):.3e} at {worst}")
+            if excess[worst] > 0:
+                bad.append(f"dQ: error {float(np.abs(g - r)[worst]):.3e} at {worst} > {bound:.3e} + D term "
+                           f"{float(dq_extra[worst]):.3e}")
+        elif err > bound:
+            bad.append(f"{name}: error {err:.3e} > {TOL_REL[dtype]:.1e} x {mag:.3e}")
+    assert not bad, f"{what}: " + "; ".join(bad)
     return errs
 
 
@@ -76,7 +116,9 @@ def test_bwd_small(case):
     say(f"fa_bwd {case}")
     ref = oracle.attention_bwd(q, k, v, do, causal=causal, scale=scale, dtype=dtype)
     got = run_fwd_bwd(q, k, v, do, causal, scale, dtype)
-    check_grads(got, ref, dtype, f"bwd {case}")
+    extra = np.stack([np.stack([d_term(q[b, h], k[b, h], v[b, h], do[b, h], np.arange(Nq), causal, scale, dtype)
+                                for h in range(H)]) for b in range(B)])
+    check_grads(got, ref, dtype, f"bwd {case}", dq_extra=extra)
     # native-type gradients are the fp32 results rounded to nearest even
     g16 = run_fwd_bwd(q, k, v, do, causal, scale, dtype, out_f32=False)
     for name, a, b in zip(("dQ", "dK", "dV"), got, g16):
@@ -132,7 +174,8 @@ def _sampled_rows(rng, n, extra):
 
 
 @pytest.mark.parametrize("name,heads", [("prefill_8k_d128", [(0, 5), (0, 30)]),
-                                        ("prefill_2k_d64", [(0, 0), (1, 7)])])
+                                        ("prefill_2k_d64", [(0, 0), (1, 7)]),
+                                        ("prefill_16k_d128_bf16", [(0, 3), (0, 12)])])
 def test_bwd_full_size_sampled(name, heads):
     # the workload at full size in the shape the benchmark times; dO from the
     # seeded generator; sampled dQ rows and dK / dV rows of a few heads
@@ -150,7 +193,11 @@ def test_bwd_full_size_sampled(name, heads):
     for b, h in heads:
         qr = _sampled_rows(rng, w.Nq, 6)
         kc = _sampled_rows(rng, w.Nkv, 6)
+        if w.spike:  # the spiked key and its neighbours
+            j = fi.spike_indices(w)[b * w.H + h]
+            kc = np.unique(np.concatenate([kc, [max(j - 1, 0), j, min(j + 1, w.Nkv - 1)]])).astype(np.int64)
         ref = oracle.attention_bwd_sampled(x["q"][b, h], x["k"][b, h], x["v"][b, h], dob[b, h], qr, kc,
                                            causal=w.causal, scale=w.scale, dtype=w.dtype)
         got = (to_np(dq[b, h])[qr], to_np(dk[b, h])[kc], to_np(dv[b, h])[kc])
-        check_grads(got, ref, w.dtype, f"{name} head ({b},{h}) sampled")
+        extra = d_term(x["q"][b, h], x["k"][b, h], x["v"][b, h], dob[b, h], qr, w.causal, w.scale, w.dtype)
+        check_grads(got, ref, w.dtype, f"{name} head ({b},{h}) sampled", dq_extra=extra)
