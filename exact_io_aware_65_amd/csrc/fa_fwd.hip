@@ -36,15 +36,20 @@
 // which is what this ordering gives the scheduler.  K therefore runs one tile
 // ahead of V in the LDS ring.
 //
-// LDS layout: rows of d 16-bit elements (row stride 2d bytes) with the 16-byte
-// chunks of each row permuted by an XOR with a function of the row.  gfx950
-// serves a ds_read_b128 in groups of 16 consecutive lanes and a ds_read_b64 /
-// ds_read_b64_tr_b16 in groups of 32, each group over 64 four-byte banks; the
-// two permutations below make every K and V operand read conflict-free.
+// LDS layout: rows of d 16-bit elements (row stride 2d bytes; d bytes for an
+// E4M3 K) with the 16-byte chunks of each row permuted by an XOR with a
+// function of the row.  gfx950 serves a ds_read_b128 in groups of 16
+// consecutive lanes and a ds_read_b64 / ds_read_b64_tr_b16 in groups of 32,
+// each group over 64 four-byte banks; the permutations below make every K and
+// V operand read conflict-free.
+//
+// Variants (template parameters): E4M3 Q and K for the first product (KF8),
+// and two key groups per query tile for grids too small to fill the chip
+// (KG = 2); both are described at the kernel.
 //
 // Softmax work per score: half a three-input max, one FMA (scale folded in,
-// base-2 domain), one exp2, one add for the fp32 row sum and half a pack to
-// 16 bits.  The accumulator is rescaled only when some row's maximum grows by
+// base-2 domain), one exp2, half a pack to 16 bits, and for the row sum one
+// fp32 add (bf16) or half a v_dot2 of the rounded P (fp16).  The accumulator is rescaled only when some row's maximum grows by
 // more than 2^8 over the value in use; otherwise the stale maximum is kept,
 // which bounds every probability by 2^8 and leaves the final O = acc / l exact,
 // because numerator and denominator share the factor.
