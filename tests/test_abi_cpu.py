@@ -289,3 +289,40 @@ def test_bwd_sizes_and_empty():
     assert fa.fa_bwd_workspace_size(-1, 1, 4) == 0
     assert bwd(B=0, q=None, k=None, v=None, o=None, dout=None, lse=None, dq=None, dk=None, dv=None, ws=None,
                ws_bytes=0)[0] == fa.FA_OK
+
+
+def test_abi_from_c(tmp_path):
+    # the header is plain C: a C99 program includes it, links the library and
+    # makes the calls that need no GPU
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    exe = tmp_path / "abi_from_c"
+    libdir = os.path.dirname(fa.LIBRARY)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_from_c.c"), "-L", libdir, "-lfa355",
+                    "-Wl,-rpath," + libdir, "-o", str(exe)], check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_last_error_is_per_thread():
+    # each thread sees the message of its own last failing call
+    import threading
+    results = {}
+
+    def worker(d):
+        for _ in range(200):
+            got, msg = fwd(d=d)
+            if f"d={d}" not in msg:
+                results[d] = msg
+                return
+        results[d] = "ok"
+
+    threads = [threading.Thread(target=worker, args=(d,)) for d in (80, 96, 112, 160)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert all(v == "ok" for v in results.values()), results
