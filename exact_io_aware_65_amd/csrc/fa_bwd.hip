@@ -163,14 +163,14 @@ void bwd_dkdv_kernel(BwdParams p)
         const auto rv = make_rsrc(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            kf[s] = as<V8>(buffer_load16(rk, key * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.sign);
-            if constexpr (!VLDS) vf[s] = as<V8>(buffer_load16(rv, key * ROWB + (16 * s + 8 * h) * 2, 0));
+            kf[s] = as<V8>(buffer_load16(rk, static_cast<uint32_t>(key) * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.sign);
+            if constexpr (!VLDS) vf[s] = as<V8>(buffer_load16(rv, static_cast<uint32_t>(key) * ROWB + (16 * s + 8 * h) * 2, 0));
         }
         if constexpr (VLDS) {
 #pragma unroll
             for (int i = 0; i < BK * DC / NT; ++i) {
                 const int ch = i * NT + tid, row = ch / DC, col = ch % DC;
-                sv[row * DC + (col ^ kswz<D>(row))] = buffer_load16(rv, (k0 + row) * ROWB + col * 16, 0);
+                sv[row * DC + (col ^ kswz<D>(row))] = buffer_load16(rv, static_cast<uint32_t>(k0 + row) * ROWB + col * 16, 0);
             }
             const int vrow = 32 * wave + c;
             va0 = vrow * ROWB + ((h ^ kswz<D>(vrow)) << 4);
@@ -362,8 +362,8 @@ void bwd_dq_kernel(BwdParams p)
         const auto rdo = make_rsrc(static_cast<const char *>(p.dout) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            qf[s] = as<V8>(buffer_load16(rq, qrow * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.sign);
-            gf[s] = as<V8>(buffer_load16(rdo, qrow * ROWB + (16 * s + 8 * h) * 2, 0));
+            qf[s] = as<V8>(buffer_load16(rq, static_cast<uint32_t>(qrow) * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.sign);
+            gf[s] = as<V8>(buffer_load16(rdo, static_cast<uint32_t>(qrow) * ROWB + (16 * s + 8 * h) * 2, 0));
         }
     }
     const bool live = qrow < p.Nq;

@@ -49,10 +49,12 @@
 //
 // Softmax work per score: half a three-input max, one FMA (scale folded in,
 // base-2 domain), one exp2, half a pack to 16 bits, and for the row sum one
-// fp32 add (bf16) or half a v_dot2 of the rounded P (fp16).  The accumulator is rescaled only when some row's maximum grows by
-// more than 2^8 over the value in use; otherwise the stale maximum is kept,
-// which bounds every probability by 2^8 and leaves the final O = acc / l exact,
-// because numerator and denominator share the factor.
+// fp32 add (bf16) or half a v_dot2 of the rounded P (fp16); the per-tile sums
+// enter the running sum through a compensated (Kahan) add.  The accumulator
+// is rescaled only when some row's maximum grows by more than 2^8 over the
+// value in use; otherwise the stale maximum is kept, which bounds every
+// probability by 2^8 and leaves the final O = acc / l exact, because
+// numerator and denominator share the factor.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -202,7 +204,10 @@ void fwd_kernel(FwdParams p)
 
     // Per-head buffer descriptors: reads past a head's last row return zeros,
     // which fills the ragged end of the last tile (those keys are masked) and
-    // the query rows past Nq.
+    // the query rows past Nq.  Offsets are unsigned 32-bit: every row of a head
+    // (< 4 GiB) fits, and for a head within a tile of 4 GiB the rows past its
+    // end wrap to rows of the same head instead.  Either way those keys get
+    // s = -inf before the row max and those query rows are never stored.
     const size_t q_head = static_cast<size_t>(bh) * p.Nq * ROWB;
     const size_t k_head = static_cast<size_t>(bh) * p.Nkv * KROWB;
     const size_t v_head = static_cast<size_t>(bh) * p.Nkv * ROWB;
@@ -220,13 +225,13 @@ void fwd_kernel(FwdParams p)
             i32x8 w;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const u32x4 x = buffer_load16(rq, qrow * ROWB + (64 * s + 32 * h + 8 * t) * 2, 0) ^ p.qsign;
+                const u32x4 x = buffer_load16(rq, static_cast<uint32_t>(qrow) * ROWB + (64 * s + 32 * h + 8 * t) * 2, 0) ^ p.qsign;
                 w[2 * t] = static_cast<int>(e4m3x4(lo_f32<T>(x[0]), hi_f32<T>(x[0]), lo_f32<T>(x[1]), hi_f32<T>(x[1])));
                 w[2 * t + 1] = static_cast<int>(e4m3x4(lo_f32<T>(x[2]), hi_f32<T>(x[2]), lo_f32<T>(x[3]), hi_f32<T>(x[3])));
             }
             qf[s] = w;
         } else {
-            const u32x4 x = buffer_load16(rq, qrow * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.qsign;
+            const u32x4 x = buffer_load16(rq, static_cast<uint32_t>(qrow) * ROWB + (16 * s + 8 * h) * 2, 0) ^ p.qsign;
             qf[s] = as<V8>(x);
         }
     }
@@ -310,7 +315,19 @@ void fwd_kernel(FwdParams p)
         for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
     float m_run = -INFINITY;  // row max (base-2 scaled) the probabilities are taken against
     float l_run = 0.f;        // running sum over this lane's half of the keys
+    float l_cmp = 0.f;        // minus the low-order part the last add dropped
     const float cs = p.c;
+
+    // Compensated (Kahan) row sum.  With millions of keys a row's per-tile
+    // sums fall near half an ulp of the running sum and plain adds round them
+    // away, always downwards; the compensation carries each add's loss into
+    // the next one.
+    auto add_l = [&](float x) {
+        const float y = x - l_cmp;
+        const float t = l_run + y;
+        l_cmp = (t - l_run) - y;
+        l_run = t;
+    };
 
     // S^T = K Q^T for the K tile in stage st (two 32-key sub-tiles).
     auto scores = [&](auto st, f32x16 (&sn)[2]) {
@@ -369,6 +386,7 @@ void fwd_kernel(FwdParams p)
             const float m_new = fmaxf(m_run, m_blk);
             const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
             l_run *= alpha;
+            l_cmp *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -410,8 +428,8 @@ void fwd_kernel(FwdParams p)
                 pf[kk][u] = as<V8>(w);
             }
         if constexpr (!kSumP) {
-            l_run += rs0 + rs1;
-            asm volatile("" : "+v"(l_run));  // keep the adds beside the exps
+            add_l(rs0 + rs1);
+            asm volatile("" : "+v"(l_run), "+v"(l_cmp));  // keep the adds beside the exps
         }
     };
     auto rowsum_p = [&](const V8 (&pf)[2][2]) {
@@ -428,7 +446,7 @@ void fwd_kernel(FwdParams p)
                     r0 = dot2<T>(w[2], ones, r0);
                     r1 = dot2<T>(w[3], ones, r1);
                 }
-            l_run += r0 + r1;
+            add_l(r0 + r1);
         }
     };
     // An empty asm statement that claims to read and rewrite P: the compiler
@@ -513,7 +531,7 @@ void fwd_kernel(FwdParams p)
     }
 
     // Epilogue: O = acc / l, LSE = ln 2 * (m + log2 l).
-    float l_tot = sum_with_other_half(l_run);
+    float l_tot = sum_with_other_half(l_run - l_cmp);
     if constexpr (KG == 2) {
         // Group 1 hands its partial result (accumulator, reference max, row
         // sum; lane by lane, so the same lane of the partner wave holds the
