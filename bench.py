@@ -54,6 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = {
     "prefill": ["exact_io_aware_65_amd/csrc/fa_fwd.hip", "exact_io_aware_65_amd/csrc/fa_device.hpp"],
     "decode": ["exact_io_aware_65_amd/csrc/fa_decode.hip", "exact_io_aware_65_amd/csrc/fa_device.hpp"],
+    "backward": ["exact_io_aware_65_amd/csrc/fa_bwd.hip", "exact_io_aware_65_amd/csrc/fa_device.hpp"],
 }
 
 
@@ -142,6 +143,11 @@ def backward_flops(B, H, Nq, Nkv, d, causal):
     return metric_flops(B, H, Nq, Nkv, d, causal) * 5 // 2
 
 
+def backward_bytes(B, H, Nq, Nkv, d, elt=2):
+    """Compulsory HBM traffic of the backward: read q, k, v, o, dO and LSE once; write dQ, dK, dV once."""
+    return B * H * (elt * (3 * Nq + 2 * Nkv) * d + 4 * Nq + elt * (Nq + 2 * Nkv) * d)
+
+
 def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
     """fa_bwd on workload w (dO from the seeded generator), each call bracketed by HIP events."""
     import statistics
@@ -177,6 +183,9 @@ def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
         "flops": flops,
         "TFLOP/s": round(flops / (mean * 1e-3) / 1e12, 2),
         "frac_of_mfma_peak": round(flops / (mean * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+        "algorithmic_bytes": backward_bytes(w.B, w.H, w.Nq, w.Nkv, w.d),
+        "workspace_bytes": nbytes,
+        "traffic": measured_traffic("backward"),
         "note": "FLOPs counted as 2.5 x the forward (five products); the kernels do seven "
                 "(S and dP are formed in both the key-block and the query-block pass)",
     }
