@@ -378,15 +378,21 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
     if (Nkv == 0) return fail(FA_ERR_INVALID, "%s: Nkv=0: attention over no keys is undefined", fn);
     if (causal && Nq > Nkv)
         return fail(FA_ERR_INVALID, "%s: causal attention needs Nq <= Nkv (got %d > %d)", fn, Nq, Nkv);
+    // With no query rows only dk = dv = 0 is written: q, o, dout, lse and dq
+    // are neither read nor written and may be NULL (as for fa_fwd).
+    const bool rows = Nq > 0;
     const void *in16[5] = {q, k, v, o, dout};
+    const bool in_needed[5] = {rows, true, true, rows, rows};
     void *outs[3] = {dq, dk, dv};
-    for (const void *ptr : in16)
-        if (!ptr || misaligned(ptr, 16))
+    const bool out_needed[3] = {rows, true, true};
+    for (int i = 0; i < 5; ++i)
+        if ((in_needed[i] && !in16[i]) || misaligned(in16[i], 16))
             return fail(FA_ERR_INVALID, "%s: q, k, v, o and dout must be non-NULL and 16-byte aligned", fn);
-    for (const void *ptr : outs)
-        if (!ptr || misaligned(ptr, 16))
+    for (int i = 0; i < 3; ++i)
+        if ((out_needed[i] && !outs[i]) || misaligned(outs[i], 16))
             return fail(FA_ERR_INVALID, "%s: dq, dk and dv must be non-NULL and 16-byte aligned", fn);
-    if (!lse || misaligned(lse, 4)) return fail(FA_ERR_INVALID, "%s: lse must be non-NULL and 4-byte aligned", fn);
+    if ((rows && !lse) || misaligned(lse, 4))
+        return fail(FA_ERR_INVALID, "%s: lse must be non-NULL and 4-byte aligned", fn);
     const unsigned __int128 bh = static_cast<unsigned __int128>(B) * H;
     const unsigned __int128 nq_el = bh * Nq * d, nkv_el = bh * Nkv * d;
     if (nq_el >= kMaxElems || nkv_el >= kMaxElems)

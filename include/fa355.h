@@ -238,6 +238,10 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, con
  * stream.  A missing, misaligned or short workspace returns FA_ERR_WORKSPACE.
  * dq, dk, dv must not overlap any input or each other.  Deterministic (no
  * atomics): the key-block and query-block passes each recompute P.
+ *
+ * Nq = 0: no query reaches any key, so dk = dv = 0 is written; q, o, dout,
+ * lse and dq are not accessed and may be NULL.  B = 0 or H = 0: FA_OK,
+ * nothing is accessed.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
            const float *lse, void *dq, void *dk, void *dv,

@@ -92,3 +92,42 @@ def test_caller_stream():
     assert torch.equal(o, ref_o) and torch.equal(lse, ref_lse)
     assert all(torch.equal(a, b) for a, b in zip(g, ref_g))
     assert torch.equal(od, od_ref)
+
+
+def test_empty_inputs():
+    # zero-size tensors (whose data pointers are NULL) through every entry point
+    dev = device()
+    q0 = torch.zeros(1, 2, 0, 64, dtype=torch.float16, device=dev)
+    k, v = (torch.randn(1, 2, 300, 64, device=dev).half() for _ in range(2))
+    say("empty inputs: fwd, fwd_fp8, decode, quantize")
+    o, lse = fa.fwd(q0, k, v, causal=True)
+    o8, lse8 = fa.fwd_fp8(q0, k, v)
+    assert o.shape == q0.shape and lse.shape == (1, 2, 0) and o8.shape == q0.shape
+    e = torch.zeros(0, 2, 9, 64, dtype=torch.bfloat16, device=dev)
+    assert fa.fwd(e, e, e)[0].shape == e.shape
+    od, ld = fa.decode(torch.zeros(0, 2, 64, dtype=torch.float16, device=dev), e.half(), e.half())
+    assert od.shape == (0, 2, 64) and ld.shape == (0, 2)
+    assert fa.quantize_e4m3(q0).shape == q0.shape
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d,causal,out_f32", [(64, False, False), (128, True, True)])
+def test_bwd_without_query_rows(d, causal, out_f32):
+    # no query reaches any key: dK = dV = 0 is written, and the query-side
+    # pointers (here NULL) are never touched
+    dev = device()
+    k, v = (torch.randn(2, 3, 300, d, device=dev).half() for _ in range(2))
+    gdt = torch.float32 if out_f32 else torch.float16
+    dk = torch.full(k.shape, float("nan"), dtype=gdt, device=dev)
+    dv = torch.full(v.shape, float("nan"), dtype=gdt, device=dev)
+    code = fa.FA_F16 | (fa.FA_OUT_F32 if out_f32 else 0)
+    say(f"fa_bwd Nq=0 d={d} causal={causal} out_f32={out_f32}")
+    fa.fa_bwd(None, k, v, None, None, None, None, dk, dv, 2, 3, 0, 300, d, causal, 0.1, code, None, 0,
+              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
+    q0 = torch.zeros(2, 3, 0, d, dtype=torch.float16, device=dev)
+    lse0 = torch.zeros(2, 3, 0, dtype=torch.float32, device=dev)
+    dq, dk2, dv2 = fa.bwd(q0, k, v, q0, q0, lse0, causal=causal, out_dtype=gdt)
+    torch.cuda.synchronize()
+    assert dq.shape == q0.shape and (dk2 == 0).all() and (dv2 == 0).all()
