@@ -484,7 +484,7 @@ def main():
     if args.gpus != 1:
         if int(os.environ.get("RANK", "0")) == 0:
             print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-                  "(the kernels shard by head with no communication; see DESIGN.md)", file=sys.stderr)
+                  "(across GPUs the kernels would shard by head, with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np  # noqa: F401
