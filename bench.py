@@ -278,6 +278,35 @@ def unfused_decode(q, k, v, scale):
     return torch.matmul(p.transpose(-1, -2).contiguous(), v).squeeze(-2)
 
 
+def measure_read_bandwidth(buf, stream, warmup, steps):
+    """HBM read rate of a plain streaming-read kernel over the device tensor buf.
+
+    The probe (libfa355_probe.so, built beside the library) reads every byte
+    once with 16-byte non-temporal loads, one contiguous chunk per workgroup:
+    the same access pattern as the decode kernels, without their arithmetic.
+    Decode is reported against it as well as against the published peak."""
+    import ctypes
+
+    import torch
+    from exact_io_aware_65_amd import build as libbuild
+    if not os.path.exists(libbuild.PROBE_LIBRARY):
+        raise RuntimeError(f"{libbuild.PROBE_LIBRARY} is missing: run python -m exact_io_aware_65_amd.build")
+    lib = ctypes.CDLL(libbuild.PROBE_LIBRARY)
+    lib.fa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_read.restype = ctypes.c_int
+    sink = torch.empty(lib.fa_probe_read_blocks() * 256, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+
+    def call():
+        rc = lib.fa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream)
+        if rc:
+            raise RuntimeError(f"fa_probe_read failed ({rc})")
+
+    mean = _event_ms(call, stream, warmup, steps)
+    return {"bytes": nbytes, "ms_mean": round(mean, 4), "GB/s": round(nbytes / (mean * 1e-3) / 1e9, 1),
+            "kernel": "read_chunks (16-byte non-temporal loads, one chunk per workgroup)"}
+
+
 def _event_ms(fn, stream, warmup, steps):
     import torch
     for _ in range(warmup):
@@ -622,6 +651,11 @@ def main():
     if run_prefill and not args.no_fp8:
         log("FP8 Q/K forward (fa_fwd_fp8) on the prefill workload")
         result["fp8_forward"] = time_fp8_forward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
+    if run_decode:
+        log("streaming-read probe over the decode K cache")
+        probe = measure_read_bandwidth(dk, stream, args.warmup, args.steps)
+        result["read_probe"] = probe
+        result["decode"]["frac_of_read_probe"] = round(gbs / probe["GB/s"], 4)
     if run_decode and not args.no_paged:
         log("decode over a paged cache (fa_decode_paged)")
         result["paged_decode"] = time_paged_decode(fa, fi, fi.WORKLOADS[PAGED], dq, dk, dv, stream, args.warmup,

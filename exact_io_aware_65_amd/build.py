@@ -3,7 +3,9 @@
     python -m exact_io_aware_65_amd.build
 
 Each source compiles to its own object (in parallel) under _build/, then the
-objects link into exact_io_aware_65_amd/libfa355.so.
+objects link into exact_io_aware_65_amd/libfa355.so.  The streaming-read probe
+that bench.py reports decode against (probe/read_bw.hip) builds into its own
+library, exact_io_aware_65_amd/libfa355_probe.so.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libfa355.so")
+PROBE_SOURCE = os.path.join(PKG, "probe", "read_bw.hip")
+PROBE_LIBRARY = os.path.join(PKG, "libfa355_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -32,7 +36,7 @@ COMMON = [
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -48,14 +52,15 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIBRARY + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIBRARY)
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
+    for lib, parts in ((LIBRARY, objs[:-1]), (PROBE_LIBRARY, objs[-1:])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *parts, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIBRARY
 
 

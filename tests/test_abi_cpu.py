@@ -326,3 +326,17 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert all(v == "ok" for v in results.values()), results
+
+
+def test_read_probe_library():
+    # the streaming-read probe bench.py reports decode against: built beside
+    # the library, exporting its two calls; bad arguments fail before any launch
+    import ctypes
+
+    from exact_io_aware_65_amd import build as libbuild
+    lib = ctypes.CDLL(libbuild.PROBE_LIBRARY)
+    lib.fa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.fa_probe_read_blocks() == 2048
+    assert lib.fa_probe_read(None, 1 << 20, 0x1000, None) == 1
+    assert lib.fa_probe_read(0x1000, 1000, 0x1000, None) == 1   # not a multiple of 16
+    assert lib.fa_probe_read(0x1008, 1 << 20, 0x1000, None) == 1  # misaligned
