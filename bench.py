@@ -307,6 +307,30 @@ def measure_read_bandwidth(buf, stream, warmup, steps):
             "kernel": "read_chunks (16-byte non-temporal loads, one chunk per workgroup)"}
 
 
+def device_name(props):
+    """The product name the driver reports in sysfs, else torch's device name."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/product_name")):
+        try:
+            with open(path) as f:
+                name = f.read().strip()
+            if name:
+                return name
+        except OSError:
+            pass
+    return props.name or getattr(props, "gcnArchName", "")
+
+
+def build_info():
+    """What build.py recorded beside the libraries (git commit of the sources)."""
+    from exact_io_aware_65_amd import build as libbuild
+    try:
+        with open(libbuild.BUILD_INFO) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return None
+
+
 def _event_ms(fn, stream, warmup, steps):
     import torch
     for _ in range(warmup):
@@ -637,8 +661,9 @@ def main():
         "decode": {"ms_mean": round(dec_mean, 4), "ms_p10": round(pct(dec_ms, 0.1), 4),
                    "ms_p50": round(pct(dec_ms, 0.5), 4), "ms_p90": round(pct(dec_ms, 0.9), 4),
                    "GB/s": round(gbs, 1), "algorithmic_bytes": d_bytes, "workspace_bytes": ws_bytes},
-        "gpu": {"name": props.name, "cus": props.multi_processor_count,
+        "gpu": {"name": device_name(props), "cus": props.multi_processor_count,
                 "arch": getattr(props, "gcnArchName", ""), "hip": torch.version.hip},
+        "build": build_info(),
         "sources": {"prefill_digest": kernel_source_digest("prefill"),
                     "decode_digest": kernel_source_digest("decode")},
     }

@@ -9,9 +9,11 @@ library, exact_io_aware_65_amd/libfa355_probe.so.
 """
 from __future__ import annotations
 
+import json
 import os
 import subprocess
 import sys
+import time
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -19,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libfa355.so")
+BUILD_INFO = os.path.join(PKG, "build_info.json")
 PROBE_SOURCE = os.path.join(PKG, "probe", "read_bw.hip")
 PROBE_LIBRARY = os.path.join(PKG, "libfa355_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -61,7 +64,24 @@ def build(verbose: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         os.replace(tmp, lib)
+    _write_build_info()
     return LIBRARY
+
+
+def _write_build_info() -> None:
+    """Record which sources the libraries were built from (git commit, and whether
+    the tree had uncommitted changes) beside them, for the benchmark's record."""
+    def git(*args):
+        try:
+            r = subprocess.run(["git", "-C", ROOT, *args], capture_output=True, text=True, timeout=20)
+            return r.stdout.strip() if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError):
+            return None
+    status = git("status", "--porcelain", "--untracked-files=no")
+    info = {"git_commit": git("rev-parse", "HEAD"), "git_dirty": None if status is None else bool(status),
+            "built_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()), "arch": ARCH}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":
