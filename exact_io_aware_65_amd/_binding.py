@@ -18,7 +18,9 @@ import ctypes
 import math
 import os
 
-LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
+# FA355_LIBRARY selects another build of the same library (the LDS-poisoning
+# debug build, for one); by default the in-tree libfa355.so.
+LIBRARY = os.environ.get("FA355_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa355.so")
 
 FA_F16 = 1
 FA_BF16 = 2

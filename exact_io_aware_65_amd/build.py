@@ -6,6 +6,12 @@ Each source compiles to its own object (in parallel) under _build/, then the
 objects link into exact_io_aware_65_amd/libfa355.so.  The streaming-read probe
 that bench.py reports decode against (probe/read_bw.hip) builds into its own
 library, exact_io_aware_65_amd/libfa355_probe.so.
+
+    python -m exact_io_aware_65_amd.build --poison-lds
+
+builds the debug variant libfa355_poison_lds.so instead: every kernel fills
+its LDS with NaN words before first use, so reads of LDS never written show up
+as NaN outputs.  Select it for a test run with FA355_LIBRARY=<path>.
 """
 from __future__ import annotations
 
@@ -24,6 +30,7 @@ LIBRARY = os.path.join(PKG, "libfa355.so")
 BUILD_INFO = os.path.join(PKG, "build_info.json")
 PROBE_SOURCE = os.path.join(PKG, "probe", "read_bw.hip")
 PROBE_LIBRARY = os.path.join(PKG, "libfa355_probe.so")
+POISON_LIBRARY = os.path.join(PKG, "libfa355_poison_lds.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -38,9 +45,9 @@ COMMON = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,6 +58,18 @@ def _compile(src: str, verbose: bool) -> str:
     if err.strip() and verbose:
         print(err, file=sys.stderr)
     return obj
+
+
+def build_poison_lds(verbose: bool = False) -> str:
+    """The debug variant of the library with LDS poisoned before use."""
+    out_dir = os.path.join(BUILD, "poison_lds")
+    os.makedirs(out_dir, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, out_dir, ("-DFA355_POISON_LDS",)), SOURCES))
+    tmp = POISON_LIBRARY + ".tmp"
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
+    os.replace(tmp, POISON_LIBRARY)
+    return POISON_LIBRARY
 
 
 def build(verbose: bool = False) -> str:
@@ -85,4 +104,7 @@ def _write_build_info() -> None:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--poison-lds" in sys.argv:
+        print(build_poison_lds(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -128,6 +128,14 @@ void bwd_dkdv_kernel(BwdParams p)
     __shared__ float sl2[2][LQ];
     __shared__ float sdd[2][LQ];
     __shared__ u32x4 sv[VLDS ? BK * DC : 1];  // the block's V [key][dim], kswz-permuted
+    if constexpr (kPoisonLds) {
+        poison_lds(sq, sizeof(sq));
+        poison_lds(sdo, sizeof(sdo));
+        poison_lds(sl2, sizeof(sl2));
+        poison_lds(sdd, sizeof(sdd));
+        poison_lds(sv, sizeof(sv));
+        __syncthreads();
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -335,6 +343,11 @@ void bwd_dq_kernel(BwdParams p)
 
     __shared__ u32x4 sk[2][TILE];  // K tiles, dswz (row and transposed reads)
     __shared__ u32x4 sv[2][TILE];  // V tiles, kswz (row reads)
+    if constexpr (kPoisonLds) {
+        poison_lds(sk, sizeof(sk));
+        poison_lds(sv, sizeof(sv));
+        __syncthreads();
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -196,6 +196,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParam
     // merge the workgroup's key streams
     __shared__ float s_m[GROUPS], s_l[GROUPS];
     __shared__ float s_acc[GROUPS][D];
+    if constexpr (kPoisonLds) {
+        // after the key loop, which uses no LDS: every thread is past it
+        poison_lds(s_m, sizeof(s_m));
+        poison_lds(s_l, sizeof(s_l));
+        poison_lds(s_acc, sizeof(s_acc));
+        __syncthreads();
+    }
     if (r == 0) {
         s_m[grp] = m;
         s_l[grp] = l;

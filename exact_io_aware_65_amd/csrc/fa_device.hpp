@@ -241,4 +241,20 @@ template <int N> __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// Debug builds (-DFA355_POISON_LDS): every kernel fills its LDS arrays with
+// all-ones words before their first use.  0xFFFFFFFF is a NaN as fp32, as
+// each fp16 or bf16 half and as each E4M3 byte, so a read of LDS that the
+// kernel never wrote, if it reaches an output, turns that output into NaN
+// and the parity tests reject it.  Normal builds compile none of this.
+#ifdef FA355_POISON_LDS
+constexpr bool kPoisonLds = true;
+#else
+constexpr bool kPoisonLds = false;
+#endif
+__device__ __forceinline__ void poison_lds(void *p, unsigned bytes)
+{
+    unsigned *w = static_cast<unsigned *>(p);
+    for (unsigned i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = ~0u;
+}
+
 }  // namespace fa355

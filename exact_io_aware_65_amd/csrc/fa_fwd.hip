@@ -172,6 +172,10 @@ void fwd_kernel(FwdParams p)
     u32x4(*const sv)[NS][TILE] = reinterpret_cast<u32x4(*)[NS][TILE]>(lds_rings + KG * NS * KTILE);
     static_assert(KG == 1 || (WGW * (DT * 16 + 2) * 64 * 4 <= KG * NS * (KTILE + TILE) * 16),
                   "the partial results of a key group fit the rings");
+    if constexpr (kPoisonLds) {
+        poison_lds(lds_rings, sizeof(lds_rings));
+        __syncthreads();
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform by construction
