@@ -1,0 +1,126 @@
+// Drives every entry point of the C ABI (include/fa355.h) through valid calls
+// and through each class of invalid argument, against the stub launchers of
+// abi_sanitize_stubs.cpp, so that the validation code runs under
+// AddressSanitizer and UndefinedBehaviorSanitizer.  Pointers are fake, aligned,
+// non-overlapping addresses: the ABI layer only checks them, and the stubs
+// never touch them.  Extreme sizes exercise the overflow guards.
+#include <climits>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa355.h"
+
+namespace {
+
+int failures = 0;
+
+void expect(int got, int want, const char *what)
+{
+    const char *msg = fa_last_error();
+    if (got != want || (want != FA_OK && (!msg || !*msg))) {
+        std::fprintf(stderr, "%s: got %s, want %s (%s)\n", what, fa_status_str(got), fa_status_str(want),
+                     msg ? msg : "(null)");
+        ++failures;
+    }
+}
+
+void *at(std::uintptr_t gib) { return reinterpret_cast<void *>(gib << 36); }  // 64 GiB apart
+
+}  // namespace
+
+int main()
+{
+    void *q = at(1), *k = at(2), *v = at(3), *o = at(4), *ws = at(6), *dq = at(7), *dk = at(8), *dv = at(9);
+    float *lse = static_cast<float *>(at(5));
+    const auto *table = static_cast<const int32_t *>(at(10));
+    const auto *lens = static_cast<const int32_t *>(at(11));
+    void *dout = at(12);
+
+    if (fa_version() != FA355_VERSION) ++failures;
+    for (int s = -1; s <= 5; ++s)
+        if (!fa_status_str(s) || !*fa_status_str(s)) ++failures;
+
+    // forward
+    expect(fa_fwd(q, k, v, o, lse, 2, 4, 300, 500, 128, 1, 0.1f, FA_F16, nullptr), FA_OK, "fwd");
+    expect(fa_fwd(q, k, v, o, nullptr, 2, 4, 300, 500, 64, 0, 0.1f, FA_BF16 | FA_OUT_F32, nullptr), FA_OK, "fwd f32");
+    expect(fa_fwd(nullptr, nullptr, nullptr, nullptr, nullptr, 2, 4, 0, 500, 128, 1, 0.1f, FA_F16, nullptr), FA_OK,
+           "fwd empty");
+    expect(fa_fwd(nullptr, k, v, o, lse, 1, 1, 64, 64, 128, 0, 0.1f, FA_F16, nullptr), FA_ERR_INVALID, "fwd null q");
+    expect(fa_fwd(q, k, v, o, lse, 1, 1, 64, 64, 96, 0, 0.1f, FA_F16, nullptr), FA_ERR_UNSUPPORTED, "fwd d=96");
+    expect(fa_fwd(q, k, v, o, lse, 1, 1, 65, 64, 128, 1, 0.1f, FA_F16, nullptr), FA_ERR_INVALID, "fwd causal");
+    expect(fa_fwd(q, k, v, o, lse, 1, 1, 64, 64, 128, 0, 1.f / 0.f, FA_F16, nullptr), FA_ERR_INVALID, "fwd scale");
+    expect(fa_fwd(q, k, v, q, lse, 1, 1, 64, 64, 128, 0, 0.1f, FA_F16, nullptr), FA_ERR_INVALID, "fwd overlap");
+    expect(fa_fwd(static_cast<char *>(q) + 8, k, v, o, lse, 1, 1, 64, 64, 128, 0, 0.1f, FA_F16, nullptr),
+           FA_ERR_INVALID, "fwd misaligned");
+    expect(fa_fwd(q, k, v, o, lse, INT_MAX, INT_MAX, INT_MAX, INT_MAX, 128, 0, 0.1f, FA_F16, nullptr),
+           FA_ERR_INVALID, "fwd 2^62");
+    expect(fa_fwd(q, k, v, o, lse, 1, 1, 64, 1 << 24, 128, 0, 0.1f, FA_F16, nullptr), FA_ERR_UNSUPPORTED,
+           "fwd 4 GiB head");
+    expect(fa_fwd(q, k, v, o, lse, -1, 1, 64, 64, 128, 0, 0.1f, FA_F16, nullptr), FA_ERR_INVALID, "fwd negative");
+    expect(fa_fwd(q, k, v, o, lse, 1, 1, 64, 64, 128, 0, 0.1f, 0x7, nullptr), FA_ERR_INVALID, "fwd dtype");
+
+    // FP8 forward and the quantiser
+    expect(fa_fwd_fp8(q, k, v, o, lse, 2, 4, 300, 500, 128, 1, 0.1f, FA_F16, nullptr), FA_OK, "fwd_fp8");
+    expect(fa_fwd_fp8(q, k, v, o, lse, 1, 1, 64, 64, 64, 0, 0.1f, 3, nullptr), FA_ERR_INVALID, "fwd_fp8 dtype");
+    expect(fa_quantize_e4m3(q, k, 4099, FA_BF16, nullptr), FA_OK, "quantize");
+    expect(fa_quantize_e4m3(nullptr, nullptr, 0, FA_F16, nullptr), FA_OK, "quantize empty");
+    expect(fa_quantize_e4m3(q, static_cast<char *>(q) + 64, 100, FA_F16, nullptr), FA_ERR_INVALID,
+           "quantize overlap");
+    expect(fa_quantize_e4m3(q, k, SIZE_MAX, FA_F16, nullptr), FA_ERR_INVALID, "quantize 2^62");
+
+    // decode
+    const std::size_t need = fa_decode_workspace_size(3, 5, 7777, 128, 0);
+    if (need == 0 || fa_decode_workspace_size(3, 5, 0, 128, 0) != 0) ++failures;
+    expect(fa_decode(q, k, v, o, lse, 3, 5, 7777, 128, 0.1f, FA_F16, 0, ws, need, nullptr), FA_OK, "decode");
+    expect(fa_decode(q, k, v, o, lse, 3, 5, 7777, 128, 0.1f, FA_F16, 0, ws, need - 16, nullptr), FA_ERR_WORKSPACE,
+           "decode short workspace");
+    expect(fa_decode(q, k, v, o, lse, 3, 5, 7777, 128, 0.1f, FA_F16, 0, k, need, nullptr), FA_ERR_WORKSPACE,
+           "decode workspace overlap");
+    expect(fa_decode(q, k, v, o, lse, 3, 5, 7777, 128, 0.1f, FA_F16, 70000, ws, 1 << 30, nullptr), FA_OK,
+           "decode more splits than keys");
+    expect(fa_decode(q, k, v, o, lse, 1, 1, 0, 128, 0.1f, FA_F16, 0, ws, need, nullptr), FA_ERR_INVALID,
+           "decode no keys");
+    expect(fa_decode(q, k, v, o, lse, INT_MAX, INT_MAX, INT_MAX, 128, 0.1f, FA_F16, 0, ws, need, nullptr),
+           FA_ERR_INVALID, "decode 2^62");
+
+    // paged decode
+    const std::size_t pneed = fa_decode_workspace_size(3, 5, 300, 64, 0);
+    expect(fa_decode_paged(q, k, v, table, lens, o, lse, 3, 5, 64, 97, 16, 19, FA_PAGED_HND, 300, 0.1f, FA_F16, 0,
+                           ws, pneed, nullptr),
+           FA_OK, "paged");
+    expect(fa_decode_paged(q, k, v, table, lens, o, lse, 3, 5, 64, 97, 16, 19, 7, 300, 0.1f, FA_F16, 0, ws, pneed,
+                           nullptr),
+           FA_ERR_INVALID, "paged layout");
+    expect(fa_decode_paged(q, k, v, table, lens, o, lse, 3, 5, 64, 97, 1 << 16, 1 << 16, FA_PAGED_NHD, 300, 0.1f,
+                           FA_F16, 0, ws, pneed, nullptr),
+           FA_ERR_INVALID, "paged capacity");
+    expect(fa_decode_paged(q, k, v, table, lens, o, lse, 3, 5, 64, 97, 16, 19, FA_PAGED_HND, 0, 0.1f, FA_F16, 0, ws,
+                           pneed, nullptr),
+           FA_ERR_INVALID, "paged max_seq_len");
+    expect(fa_decode_paged(q, k, v, table, lens, o, lse, 3, 5, 64, INT_MAX, INT_MAX, 1, FA_PAGED_HND, 300, 0.1f,
+                           FA_F16, 0, ws, pneed, nullptr),
+           FA_ERR_INVALID, "paged huge pages");
+
+    // backward
+    const std::size_t bneed = fa_bwd_workspace_size(2, 4, 300);
+    expect(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, 2, 4, 300, 500, 128, 1, 0.1f, FA_F16, ws, bneed, nullptr), FA_OK,
+           "bwd");
+    expect(fa_bwd(nullptr, k, v, nullptr, nullptr, nullptr, nullptr, dk, dv, 2, 4, 0, 500, 64, 1, 0.1f,
+                  FA_BF16 | FA_OUT_F32, nullptr, 0, nullptr),
+           FA_OK, "bwd no query rows");
+    expect(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, 2, 4, 300, 500, 128, 1, 0.1f, FA_F16, nullptr, 0, nullptr),
+           FA_ERR_WORKSPACE, "bwd no workspace");
+    expect(fa_bwd(q, k, v, o, dout, lse, dq, dq, dv, 2, 4, 300, 500, 128, 1, 0.1f, FA_F16, ws, bneed, nullptr),
+           FA_ERR_INVALID, "bwd outputs overlap");
+    expect(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, INT_MAX, INT_MAX, INT_MAX, INT_MAX, 128, 0, 0.1f, FA_F16, ws,
+                  bneed, nullptr),
+           FA_ERR_INVALID, "bwd 2^62");
+
+    if (failures) {
+        std::fprintf(stderr, "%d failures\n", failures);
+        return 1;
+    }
+    std::puts("ABI validation ran clean");
+    return 0;
+}

@@ -340,3 +340,26 @@ def test_read_probe_library():
     assert lib.fa_probe_read(None, 1 << 20, 0x1000, None) == 1
     assert lib.fa_probe_read(0x1000, 1000, 0x1000, None) == 1   # not a multiple of 16
     assert lib.fa_probe_read(0x1008, 1 << 20, 0x1000, None) == 1  # misaligned
+
+
+def test_abi_validation_under_sanitizers(tmp_path):
+    # the ABI layer (fa_abi.cpp) built for the host with g++ under
+    # AddressSanitizer and UndefinedBehaviorSanitizer, against stub launchers:
+    # every entry point, valid calls and each class of invalid argument,
+    # including sizes at INT_MAX that exercise the overflow guards
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(os.path.dirname(here), "exact_io_aware_65_amd", "csrc")
+    exe = str(tmp_path / "abi_sanitize")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    "-I", os.path.join(os.path.dirname(here), "include"), "-I", csrc,
+                    os.path.join(here, "c", "abi_sanitize.cpp"), os.path.join(here, "c", "abi_sanitize_stubs.cpp"),
+                    os.path.join(csrc, "fa_abi.cpp"), "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1"))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "ran clean" in r.stdout
