@@ -32,6 +32,7 @@
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace fa355 {
@@ -233,25 +234,80 @@ struct CombineParams {
     int splits;
 };
 
+// One workgroup per (batch, head).  All threads first take the largest
+// partial LSE together; then group g of the kCombThreads / D groups of D
+// threads (one per dimension) sums splits g, g + groups, ... with four loads
+// in flight, and the groups' sums are added through LDS.  Few heads with many
+// splits (a small batch over a long cache) thus cost a few microseconds
+// instead of a serial walk over the splits.
+constexpr int kCombThreads = 512;
+
 template <int D, typename TO>
-__global__ __launch_bounds__(D) void decode_combine_kernel(CombineParams p)
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(CombineParams p)
 {
-    const int bh = blockIdx.x, d = threadIdx.x;
+    constexpr int G = kCombThreads / D;  // split groups
+    constexpr int WAVES = kCombThreads / 64;
+    __shared__ float s_max[WAVES];
+    __shared__ float s_num[G][D];
+    __shared__ float s_den[G];
+    if constexpr (kPoisonLds) {
+        poison_lds(s_max, sizeof(s_max));
+        poison_lds(s_num, sizeof(s_num));
+        poison_lds(s_den, sizeof(s_den));
+        __syncthreads();
+    }
+    const int bh = blockIdx.x, t = threadIdx.x, d = t % D, g = t / D;
     const float *L = p.ws_lse + static_cast<size_t>(bh) * p.splits;
     const float *O = p.ws_o + static_cast<size_t>(bh) * p.splits * D + d;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, L[s]);
+
+    float m = -INFINITY;
+    for (int s = t; s < p.splits; s += kCombThreads) m = fmaxf(m, L[s]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((t & 63) == 0) s_max[t >> 6] = m;
+    __syncthreads();
+    float M = s_max[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_max[w]);
     const float Mref = M == -INFINITY ? 0.f : M;  // every chunk empty: O = 0/0 below
+
     float den = 0.f, num = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-        const float wgt = fast_exp2(L[s] - Mref);
-        den += wgt;
-        num += wgt * O[static_cast<size_t>(s) * D];
+    int s = g;
+    for (; s + 3 * G < p.splits; s += 4 * G) {
+        float w[4], o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            w[u] = L[s + u * G];
+            o[u] = O[static_cast<size_t>(s + u * G) * D];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wu = fast_exp2(w[u] - Mref);
+            den += wu;
+            num += wu * o[u];
+        }
     }
-    // den == 0 only when every chunk was empty (a paged sequence of length 0):
-    // attention over no key gives O = 0 and LSE = ln 0 = -inf
-    static_cast<TO *>(p.o)[static_cast<size_t>(bh) * D + d] = static_cast<TO>(den > 0.f ? num / den : 0.f);
-    if (d == 0 && p.lse) p.lse[bh] = den > 0.f ? (M + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
+    for (; s < p.splits; s += G) {
+        const float wu = fast_exp2(L[s] - Mref);
+        den += wu;
+        num += wu * O[static_cast<size_t>(s) * D];
+    }
+    s_num[g][d] = num;
+    if (d == 0) s_den[g] = den;  // the same for every dimension of the group
+    __syncthreads();
+    if (g == 0) {
+        num = s_num[0][d];
+        den = s_den[0];
+#pragma unroll
+        for (int q = 1; q < G; ++q) {
+            num += s_num[q][d];
+            den += s_den[q];
+        }
+        // den == 0 only when every chunk was empty (a paged sequence of length
+        // 0): attention over no key gives O = 0 and LSE = ln 0 = -inf
+        static_cast<TO *>(p.o)[static_cast<size_t>(bh) * D + d] = static_cast<TO>(den > 0.f ? num / den : 0.f);
+        if (d == 0 && p.lse) p.lse[bh] = den > 0.f ? (M + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
+    }
 }
 
 template <int D, typename T, bool PAGED>
@@ -297,9 +353,9 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream)
     cp.lse = a.lse;
     cp.splits = a.splits;
     if (a.out_f32)
-        hipLaunchKernelGGL((decode_combine_kernel<D, float>), dim3(n_bh), dim3(D), 0, stream, cp);
+        hipLaunchKernelGGL((decode_combine_kernel<D, float>), dim3(n_bh), dim3(kCombThreads), 0, stream, cp);
     else
-        hipLaunchKernelGGL((decode_combine_kernel<D, T>), dim3(n_bh), dim3(D), 0, stream, cp);
+        hipLaunchKernelGGL((decode_combine_kernel<D, T>), dim3(n_bh), dim3(kCombThreads), 0, stream, cp);
     return hipGetLastError();
 }
 
@@ -315,16 +371,19 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 
 int decode_auto_splits(int B, int H, int Nkv, int /*d*/)
 {
-    // About 2K keys per split, and enough workgroups to give every CU several.
+    // Measured on MI355X (one process, interleaved): a long stream per
+    // workgroup is cheapest, so the split count only has to give the chip
+    // enough workgroups.  Four splits per head from 64 to 512 heads (the
+    // 16 x 32 x 32K cache: 7.03 TB/s against 6.92 with 2K keys per split),
+    // about 256 workgroups when there are fewer heads (one head of 1M keys:
+    // 6.1 TB/s at 256 splits, 5.1 at 1024), one split once the heads alone
+    // give about 2048 workgroups, and never fewer than ~128 keys per split.
     const long long n_bh = static_cast<long long>(B) * H;
-    long long s = (Nkv + 2047) / 2048;
-    const long long want_blocks = 2048;
-    if (n_bh * s < want_blocks) s = (want_blocks + n_bh - 1) / n_bh;
-    const long long max_s = (Nkv + 127) / 128;  // keep at least ~128 keys per split
-    if (s > max_s) s = max_s;
-    if (s > 256) s = 256;
-    if (s < 1) s = 1;
-    return static_cast<int>(s);
+    if (n_bh < 1 || Nkv < 1) return 1;
+    long long s = std::max<long long>((256 + n_bh - 1) / n_bh, 4);
+    s = std::min<long long>(s, std::max<long long>((2048 + n_bh - 1) / n_bh, 1));
+    s = std::min<long long>(s, (Nkv + 127) / 128);
+    return static_cast<int>(std::max<long long>(s, 1));
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream)
