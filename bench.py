@@ -27,6 +27,7 @@ host's cores; it is a reference point, not the target.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-other] [--no-fp8] [--no-paged]
     python bench.py --sweep [--steps K] [--warmup W]   # fused vs unfused over sequence length
+    python bench.py --map [--steps K] [--warmup W]     # fused kernels over N, d, mask, type
 """
 from __future__ import annotations
 
@@ -423,6 +424,72 @@ def run_sweep(warmup, steps):
     return out
 
 
+MAP_TOKENS = 1 << 18                     # B*H*N of every forward point (heads scale with 1/N)
+MAP_PREFILL = (1024, 2048, 4096, 8192, 16384, 32768)
+MAP_DECODE = ((16, 32, 4096), (16, 32, 16384), (16, 32, 65536), (16, 32, 131072),  # (B, H, cache length)
+              (4, 8, 131072), (1, 8, 32768), (1, 1, 1 << 20))
+
+
+def run_map(warmup, steps):
+    """Fused kernels only, over shapes: fa_fwd and fa_fwd_fp8 for N in
+    MAP_PREFILL, d in {64, 128}, causal or not, fp16 and bf16, with B = 1 and
+    H = MAP_TOKENS / N; fa_decode for the (B, H, cache length) points of
+    MAP_DECODE, d in {64, 128}, fp16.  Inputs are drawn on the device (timing
+    only)."""
+    import torch
+
+    import exact_io_aware_65_amd as fa
+    import fa_inputs as fi
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    out = {"prefill": [], "decode": []}
+    for n in MAP_PREFILL:
+        H = MAP_TOKENS // n
+        for d in (64, 128):
+            for dtype in ("f16", "bf16"):
+                q, k, v = (fi.device_normals((1, H, n, d), dtype, 100 + t, dev) for t in range(3))
+                k8 = fa.quantize_e4m3(k)
+                o = torch.empty_like(q)
+                lse = torch.empty((1, H, n), dtype=torch.float32, device=dev)
+                code = fa.FA_F16 if dtype == "f16" else fa.FA_BF16
+                scale = 1.0 / math.sqrt(d)
+                for causal in (True, False):
+                    t16 = _event_ms(lambda: fa.fa_fwd(q, k, v, o, lse, 1, H, n, n, d, causal, scale, code, sp),
+                                    stream, warmup, steps)
+                    t8 = _event_ms(lambda: fa.fa_fwd_fp8(q, k8, v, o, lse, 1, H, n, n, d, causal, scale, code, sp),
+                                   stream, warmup, steps)
+                    flops = metric_flops(1, H, n, n, d, causal)
+                    out["prefill"].append({"N": n, "H": H, "d": d, "dtype": dtype, "causal": causal,
+                                           "ms": round(t16, 4), "TFLOP/s": round(flops / (t16 * 1e-3) / 1e12, 1),
+                                           "fp8_ms": round(t8, 4),
+                                           "fp8_TFLOP/s": round(flops / (t8 * 1e-3) / 1e12, 1)})
+                    print(f"[map] fwd N={n} H={H} d={d} {dtype} {'causal' if causal else 'full'}: "
+                          f"{flops / (t16 * 1e-3) / 1e12:.0f} / fp8 {flops / (t8 * 1e-3) / 1e12:.0f} TFLOP/s",
+                          file=sys.stderr, flush=True)
+                q = k = v = k8 = o = lse = None
+                torch.cuda.empty_cache()
+    for B, H, n in MAP_DECODE:
+        for d in (64, 128):
+            q = fi.device_normals((B, H, d), "f16", 200, dev)
+            k, v = (fi.device_normals((B, H, n, d), "f16", 201 + t, dev) for t in range(2))
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+            nbytes = fa.fa_decode_workspace_size(B, H, n, d, 0)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            scale = 1.0 / math.sqrt(d)
+            t = _event_ms(lambda: fa.fa_decode(q, k, v, o, lse, B, H, n, d, scale, fa.FA_F16, 0, ws, nbytes, sp),
+                          stream, warmup, steps)
+            nb = algorithmic_bytes(B, H, 1, n, d)
+            out["decode"].append({"Nkv": n, "B": B, "H": H, "d": d, "splits": fa.fa_decode_num_splits(B, H, n, d),
+                                  "ms": round(t, 4), "GB/s": round(nb / (t * 1e-3) / 1e9, 1)})
+            print(f"[map] decode B={B} H={H} Nkv={n} d={d}: {nb / (t * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+            q = k = v = o = lse = ws = None
+            torch.cuda.empty_cache()
+    return out
+
+
 OTHER_PREFILL = ("prefill_2k_d64", "prefill_16k_d128_bf16")
 
 
@@ -519,6 +586,8 @@ def main():
                     help="skip the separate timing of decode over a paged cache (fa_decode_paged)")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the speed-vs-length sweep of the fused kernels against the unfused baseline")
+    ap.add_argument("--map", action="store_true",
+                    help="only run the speed map of the fused kernels over sequence length, head dim, mask and type")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the timing of the other prefill workloads (2K d64, 16K d128 bf16)")
     ap.add_argument("--no-fp8", action="store_true",
@@ -533,6 +602,13 @@ def main():
         res = run_sweep(max(1, args.warmup), max(1, args.steps))
         print(json.dumps({"metric": "fused vs unfused attention time over sequence length", "unit": "ms",
                           "higher_is_better": False, "dtype": "f16", "data": "synthetic", "sweep": res}), flush=True)
+        return
+    if args.map:
+        if args.gpus != 1:
+            sys.exit("bench.py --map measures one GPU only")
+        res = run_map(max(1, args.warmup), max(1, args.steps))
+        print(json.dumps({"metric": "fused kernel speed over shapes", "unit": "TFLOP/s, GB/s",
+                          "higher_is_better": True, "data": "synthetic", "map": res}), flush=True)
         return
     if args.gpus != 1:
         if int(os.environ.get("RANK", "0")) == 0:

@@ -192,6 +192,19 @@ def torch_to_bits(t) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# timing-only inputs
+
+def device_normals(shape, dtype: str, seed: int, device):
+    """Standard normal samples drawn on the device by torch's seeded generator
+    and rounded to the 16-bit type: the same distribution as the host
+    generator above, for performance maps over many shapes where drawing on
+    the host would dominate.  No parity test and no oracle input uses them."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch_dtype(dtype))
+
+
 # paged caches
 
 @dataclass(frozen=True)
