@@ -19,7 +19,9 @@ reported in its own "backward" object, the other two prefill workloads
 rounded to E4M3 for the first product) on the prefill workload in an
 "fp8_forward" object, and decode over a paged cache (fa_decode_paged: the
 decode cache scattered into a shuffled pool of 16-key pages) in a
-"paged_decode" object; none of them is part of `value`.
+"paged_decode" object; none of them is part of `value`.  A plain
+streaming-read kernel (libfa355_probe) timed over the decode K cache gives
+the measured HBM read rate decode is also compared against ("read_probe").
 
 The CPU baseline is the fp64 oracle (plain standard attention that
 materialises the score matrix) timed on a sample of the prefill heads on the
