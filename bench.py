@@ -433,7 +433,7 @@ MAP_DECODE = ((16, 32, 4096), (16, 32, 16384), (16, 32, 65536), (16, 32, 131072)
 
 
 def run_map(warmup, steps):
-    """Fused kernels only, over shapes: fa_fwd and fa_fwd_fp8 for N in
+    """Fused kernels only, over shapes: fa_fwd, fa_fwd_fp8 and fa_bwd for N in
     MAP_PREFILL, d in {64, 128}, causal or not, fp16 and bf16, with B = 1 and
     H = MAP_TOKENS / N; fa_decode for the (B, H, cache length) points of
     MAP_DECODE, d in {64, 128}, fp16.  Inputs are drawn on the device (timing
@@ -450,9 +450,11 @@ def run_map(warmup, steps):
         H = MAP_TOKENS // n
         for d in (64, 128):
             for dtype in ("f16", "bf16"):
-                q, k, v = (fi.device_normals((1, H, n, d), dtype, 100 + t, dev) for t in range(3))
+                q, k, v, do = (fi.device_normals((1, H, n, d), dtype, 100 + t, dev) for t in range(4))
                 k8 = fa.quantize_e4m3(k)
                 o = torch.empty_like(q)
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                bws = torch.empty(max(fa.fa_bwd_workspace_size(1, H, n), 16), dtype=torch.uint8, device=dev)
                 lse = torch.empty((1, H, n), dtype=torch.float32, device=dev)
                 code = fa.FA_F16 if dtype == "f16" else fa.FA_BF16
                 scale = 1.0 / math.sqrt(d)
@@ -461,15 +463,21 @@ def run_map(warmup, steps):
                                     stream, warmup, steps)
                     t8 = _event_ms(lambda: fa.fa_fwd_fp8(q, k8, v, o, lse, 1, H, n, n, d, causal, scale, code, sp),
                                    stream, warmup, steps)
+                    fa.fa_fwd(q, k, v, o, lse, 1, H, n, n, d, causal, scale, code, sp)  # O and LSE of this mask
+                    tb = _event_ms(lambda: fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, 1, H, n, n, d, causal, scale,
+                                                     code, bws, bws.numel(), sp), stream, warmup, steps)
                     flops = metric_flops(1, H, n, n, d, causal)
+                    bflops = backward_flops(1, H, n, n, d, causal)
                     out["prefill"].append({"N": n, "H": H, "d": d, "dtype": dtype, "causal": causal,
                                            "ms": round(t16, 4), "TFLOP/s": round(flops / (t16 * 1e-3) / 1e12, 1),
                                            "fp8_ms": round(t8, 4),
-                                           "fp8_TFLOP/s": round(flops / (t8 * 1e-3) / 1e12, 1)})
+                                           "fp8_TFLOP/s": round(flops / (t8 * 1e-3) / 1e12, 1),
+                                           "bwd_ms": round(tb, 4),
+                                           "bwd_TFLOP/s": round(bflops / (tb * 1e-3) / 1e12, 1)})
                     print(f"[map] fwd N={n} H={H} d={d} {dtype} {'causal' if causal else 'full'}: "
-                          f"{flops / (t16 * 1e-3) / 1e12:.0f} / fp8 {flops / (t8 * 1e-3) / 1e12:.0f} TFLOP/s",
-                          file=sys.stderr, flush=True)
-                q = k = v = k8 = o = lse = None
+                          f"{flops / (t16 * 1e-3) / 1e12:.0f} / fp8 {flops / (t8 * 1e-3) / 1e12:.0f} / "
+                          f"bwd {bflops / (tb * 1e-3) / 1e12:.0f} TFLOP/s", file=sys.stderr, flush=True)
+                q = k = v = do = k8 = o = lse = dq = dk = dv = bws = None
                 torch.cuda.empty_cache()
     for B, H, n in MAP_DECODE:
         for d in (64, 128):
