@@ -131,3 +131,44 @@ def test_bwd_without_query_rows(d, causal, out_f32):
     dq, dk2, dv2 = fa.bwd(q0, k, v, q0, q0, lse0, causal=causal, out_dtype=gdt)
     torch.cuda.synchronize()
     assert dq.shape == q0.shape and (dk2 == 0).all() and (dv2 == 0).all()
+
+
+def test_concurrent_callers():
+    # the library keeps no shared mutable state (the last-error text is per
+    # thread): four host threads, each on its own stream, calling the forward,
+    # decode and backward at once give the bits of the same calls made one by one
+    import threading
+    cases = []
+    for i in range(4):
+        q, k, v = _qkv(100 + i, 1, 4, 200 + 37 * i, 300 + 41 * i, 64 if i % 2 else 128)
+        cases.append((q, k, v))
+
+    def run(case):
+        q, k, v = case
+        o, lse = fa.fwd(q, k, v, causal=True)
+        od, ld = fa.decode(q[:, :, -1].contiguous(), k, v)
+        g = fa.bwd(q, k, v, o, q, lse, causal=True)
+        return (o, lse, od, ld) + tuple(g)
+
+    say("four threads on four streams")
+    ref = [run(c) for c in cases]
+    torch.cuda.synchronize()
+    out = [None] * len(cases)
+    streams = [torch.cuda.Stream() for _ in cases]
+    start = threading.Barrier(len(cases))
+
+    def worker(i):
+        with torch.cuda.stream(streams[i]):
+            start.wait()
+            for _ in range(3):
+                out[i] = run(cases[i])
+        streams[i].synchronize()
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for r, o in zip(ref, out):
+        assert all(torch.equal(a, b) for a, b in zip(r, o))
