@@ -588,8 +588,9 @@ void fwd_kernel(FwdParams p)
 }
 
 // Launch shapes: 8 waves (256 rows per workgroup, one workgroup per CU) when
-// the grid gives every CU such a workgroup, else 4 waves (128 rows, two
-// workgroups per CU); both with a 2-stage ring.  Measured on the 8K d=128
+// the grid gives every CU such a workgroup; two 4-wave key groups on 128 rows
+// when even 128-row tiles leave CUs idle; else 4 waves (128 rows, two
+// workgroups per CU); all with a 2-stage ring.  Measured on the 8K d=128
 // causal workload, deeper rings (3 or 4 stages) were no faster: a step's
 // loads already land within the step, and the chip is power-bound there.
 constexpr int kCUs = 256;
