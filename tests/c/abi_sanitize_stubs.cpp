@@ -37,6 +37,8 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t)
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t)
 {
     expect(a.B > 0 && a.H > 0 && a.splits > 0 && a.chunk > 0 && a.ws_o && a.ws_lse, "decode launch without splits");
+    const std::size_t parts = static_cast<std::size_t>(a.B) * a.H * a.splits;
+    expect(a.ws_lse == a.ws_o + parts * a.d, "decode partial LSEs misplaced");
     return hipSuccess;
 }
 
