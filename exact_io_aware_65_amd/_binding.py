@@ -76,11 +76,13 @@ def library() -> ctypes.CDLL:
 
 
 def _addr(x):
-    """Device address of a tensor (or an int / None passed through)."""
+    """Device address of a tensor, handle of a torch stream (an int or None passes through)."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if hasattr(x, "cuda_stream"):
+        return x.cuda_stream
     return x.data_ptr()
 
 
@@ -171,6 +173,12 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _check_rank(dims, **tensors):
+    for name, t in tensors.items():
+        if t.dim() != dims:
+            raise ValueError(f"{name} must have {dims} dimensions, got shape {tuple(t.shape)}")
+
+
 def _check_inputs(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -190,6 +198,7 @@ def fwd(q, k, v, *, causal=False, scale=None, out_dtype=None, with_lse=True):
     torch.float32 to get O in fp32, else O has q's dtype."""
     import torch
     _check_inputs(q, k, v)
+    _check_rank(4, q=q, k=k, v=v)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
     if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
@@ -204,7 +213,8 @@ def fwd(q, k, v, *, causal=False, scale=None, out_dtype=None, with_lse=True):
         odt = torch.float32
     o = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if with_lse else None
-    fa_fwd(q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, code, _stream(q.device))
+    with torch.cuda.device(q.device):
+        fa_fwd(q, k, v, o, lse, B, H, Nq, Nkv, d, causal, scale, code, _stream(q.device))
     return o, lse
 
 
@@ -214,7 +224,8 @@ def quantize_e4m3(x):
     if not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous GPU tensor")
     y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    fa_quantize_e4m3(x, y, x.numel(), _dtype_code(x), _stream(x.device))
+    with torch.cuda.device(x.device):
+        fa_quantize_e4m3(x, y, x.numel(), _dtype_code(x), _stream(x.device))
     return y
 
 
@@ -236,6 +247,7 @@ def fwd_fp8(q, k, v, *, causal=False, scale=None, out_dtype=None, with_lse=True)
         k8 = k
     else:
         raise TypeError(f"k must be float16, bfloat16, uint8 or float8_e4m3fn, got {k.dtype}")
+    _check_rank(4, q=q, k=k, v=v)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
     if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
@@ -250,7 +262,8 @@ def fwd_fp8(q, k, v, *, causal=False, scale=None, out_dtype=None, with_lse=True)
         odt = torch.float32
     o = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if with_lse else None
-    fa_fwd_fp8(q, k8, v, o, lse, B, H, Nq, Nkv, d, causal, scale, code, _stream(q.device))
+    with torch.cuda.device(q.device):
+        fa_fwd_fp8(q, k8, v, o, lse, B, H, Nq, Nkv, d, causal, scale, code, _stream(q.device))
     return o, lse
 
 
@@ -260,6 +273,7 @@ def decode(q, k, v, *, scale=None, num_splits=0, out_dtype=None):
     Returns (o, lse) with o shaped like q."""
     import torch
     _check_inputs(q, k, v)
+    _check_rank(4, k=k, v=v)
     B, H, Nkv, d = k.shape
     if v.shape != k.shape or q.numel() != B * H * d or q.shape[:2] != (B, H):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
@@ -275,7 +289,8 @@ def decode(q, k, v, *, scale=None, num_splits=0, out_dtype=None):
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     nbytes = fa_decode_workspace_size(B, H, Nkv, d, num_splits)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, code, num_splits, ws, nbytes, _stream(q.device))
+    with torch.cuda.device(q.device):
+        fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, code, num_splits, ws, nbytes, _stream(q.device))
     return o, lse
 
 
@@ -293,6 +308,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, layout="hnd", ma
     _check_inputs(q, k_pages, v_pages)
     if q.dim() != 3:
         raise ValueError(f"q must be [B, H, d], got {tuple(q.shape)}")
+    _check_rank(4, k_pages=k_pages, v_pages=v_pages)
     B, H, d = q.shape
     if layout == "hnd":
         num_pages, Hk, page_size, dk = k_pages.shape
@@ -323,8 +339,9 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, *, layout="hnd", ma
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     nbytes = fa_decode_workspace_size(B, H, max_seq_len, d, num_splits)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    fa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, B, H, d, num_pages, page_size, max_pages,
-                    code_layout, max_seq_len, scale, code, num_splits, ws, nbytes, _stream(q.device))
+    with torch.cuda.device(q.device):
+        fa_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, B, H, d, num_pages, page_size,
+                        max_pages, code_layout, max_seq_len, scale, code, num_splits, ws, nbytes, _stream(q.device))
     return o, lse
 
 
@@ -335,6 +352,7 @@ def bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, out_dtype=None):
     have q's dtype."""
     import torch
     _check_inputs(q, k, v)
+    _check_rank(4, q=q, k=k, v=v)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
     if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d):
@@ -342,8 +360,8 @@ def bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, out_dtype=None):
     for name, t in (("o", o), ("dout", dout)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous tensor like q")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     code = _dtype_code(q)
     gdt = q.dtype
@@ -357,5 +375,7 @@ def bwd(q, k, v, o, dout, lse, *, causal=False, scale=None, out_dtype=None):
     dv = torch.empty(v.shape, dtype=gdt, device=q.device)
     nbytes = fa_bwd_workspace_size(B, H, Nq)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, causal, scale, code, ws, nbytes, _stream(q.device))
+    with torch.cuda.device(q.device):
+        fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nkv, d, causal, scale, code, ws, nbytes,
+               _stream(q.device))
     return dq, dk, dv

@@ -103,14 +103,22 @@ int check_tensors(const char *fn, const void *q, const void *k, const void *v, c
     return FA_OK;
 }
 
-// Split count actually used for (Nkv, requested); each split holds >= 1 key.
+// Split count actually used for (Nkv >= 1, requested); each split holds >= 1
+// key.  The sums are formed in 64 bits: Nkv and the request may both be near
+// INT_MAX.
 void resolve_splits(int B, int H, int Nkv, int d, int requested, int *splits, int *chunk)
 {
-    int s = requested > 0 ? requested : fa355::decode_auto_splits(B, H, Nkv, d);
+    long long s = requested > 0 ? requested : fa355::decode_auto_splits(B, H, Nkv, d);
     if (s > Nkv) s = Nkv;
-    const int c = (Nkv + s - 1) / s;
-    *chunk = c;
-    *splits = (Nkv + c - 1) / c;
+    const long long c = (static_cast<long long>(Nkv) + s - 1) / s;
+    *chunk = static_cast<int>(c);
+    *splits = static_cast<int>((Nkv + c - 1) / c);
+}
+
+// Workgroups of a split decode: one per (b, h, split), at most INT_MAX.
+bool decode_grid_fits(int B, int H, int splits)
+{
+    return static_cast<unsigned __int128>(B) * H * splits <= 0x7fffffffU;
 }
 
 }  // namespace
@@ -210,6 +218,7 @@ size_t fa_decode_workspace_size(int B, int H, int Nkv, int d, int num_splits)
     if (B == 0 || H == 0) return 0;
     int splits, chunk;
     resolve_splits(B, H, Nkv, d, num_splits, &splits, &chunk);
+    if (!decode_grid_fits(B, H, splits)) return 0;  // fa_decode rejects such a call
     return fa355::decode_workspace_bytes(B, H, splits, d);
 }
 
@@ -243,9 +252,9 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
         return fail(FA_ERR_UNSUPPORTED, "%s: one head of k or v exceeds 4 GiB", fn);
     int splits, chunk;
     resolve_splits(B, H, Nkv, d, num_splits, &splits, &chunk);
-    const long long blocks = static_cast<long long>(B) * H * splits;
-    if (blocks > 0x7fffffffLL)
-        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+    if (!decode_grid_fits(B, H, splits))
+        return fail(FA_ERR_UNSUPPORTED, "%s: B*H*splits = %d*%d*%d workgroups exceed the grid limit", fn, B, H,
+                    splits);
     const size_t need = fa355::decode_workspace_bytes(B, H, splits, d);
     if (!workspace || misaligned(workspace, 16) || workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)",
@@ -311,9 +320,9 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, con
 
     int splits, chunk;
     resolve_splits(B, H, max_seq_len, d, num_splits, &splits, &chunk);
-    const long long blocks = static_cast<long long>(B) * H * splits;
-    if (blocks > 0x7fffffffLL)
-        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+    if (!decode_grid_fits(B, H, splits))
+        return fail(FA_ERR_UNSUPPORTED, "%s: B*H*splits = %d*%d*%d workgroups exceed the grid limit", fn, B, H,
+                    splits);
     const size_t need = fa355::decode_workspace_bytes(B, H, splits, d);
     if (!workspace || misaligned(workspace, 16) || workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)",
@@ -358,6 +367,8 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, con
 size_t fa_bwd_workspace_size(int B, int H, int Nq)
 {
     if (B < 0 || H < 0 || Nq < 0) return 0;
+    // fa_bwd rejects B*H*Nq*d >= 2^62, so with d >= 64 no valid call has more rows
+    if (static_cast<unsigned __int128>(B) * H * Nq >= (kMaxElems >> 6)) return 0;
     return fa355::bwd_workspace_bytes(B, H, Nq);
 }
 

@@ -382,7 +382,7 @@ int decode_auto_splits(int B, int H, int Nkv, int /*d*/)
     if (n_bh < 1 || Nkv < 1) return 1;
     long long s = std::max<long long>((256 + n_bh - 1) / n_bh, 4);
     s = std::min<long long>(s, std::max<long long>((2048 + n_bh - 1) / n_bh, 1));
-    s = std::min<long long>(s, (Nkv + 127) / 128);
+    s = std::min<long long>(s, (static_cast<long long>(Nkv) + 127) / 128);
     return static_cast<int>(std::max<long long>(s, 1));
 }
 

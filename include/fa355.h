@@ -162,7 +162,8 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int Nkv, int d, float scale, int dtype, int num_splits,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace fa_decode needs for these arguments (0 if they are invalid). */
+/* Bytes of workspace fa_decode needs for these arguments (0 if they are invalid,
+ * or if B * H * splits exceeds INT_MAX, which fa_decode rejects). */
 size_t fa_decode_workspace_size(int B, int H, int Nkv, int d, int num_splits);
 
 /* The split count fa_decode uses for num_splits = 0 (0 if the arguments are invalid). */
@@ -248,7 +249,9 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
            int B, int H, int Nq, int Nkv, int d, int causal, float scale, int dtype,
            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace fa_bwd needs (0 if the arguments are invalid). */
+/* Bytes of workspace fa_bwd needs: 0 for Nq = 0 (no workspace is used), and 0
+ * if the arguments are invalid or B * H * Nq >= 2^56 (fa_bwd rejects every
+ * such call: its tensors would exceed 2^62 elements). */
 size_t fa_bwd_workspace_size(int B, int H, int Nq);
 
 /* Static, human-readable name of a status code. */

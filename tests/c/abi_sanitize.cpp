@@ -101,6 +101,10 @@ int main()
     expect(fa_decode_paged(q, k, v, table, lens, o, lse, 3, 5, 64, INT_MAX, INT_MAX, 1, FA_PAGED_HND, 300, 0.1f,
                            FA_F16, 0, ws, pneed, nullptr),
            FA_ERR_INVALID, "paged huge pages");
+    // 2^40 heads in 2^30 one-key splits: 2^70 workgroups, counted without overflow
+    expect(fa_decode_paged(q, k, v, table, lens, o, lse, 1 << 20, 1 << 20, 64, 1, 1, 1 << 30, FA_PAGED_HND, 1 << 30,
+                           0.1f, FA_F16, 1 << 30, ws, SIZE_MAX, nullptr),
+           FA_ERR_UNSUPPORTED, "paged grid 2^70");
 
     // backward
     const std::size_t bneed = fa_bwd_workspace_size(2, 4, 300);
@@ -116,6 +120,19 @@ int main()
     expect(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, INT_MAX, INT_MAX, INT_MAX, INT_MAX, 128, 0, 0.1f, FA_F16, ws,
                   bneed, nullptr),
            FA_ERR_INVALID, "bwd 2^62");
+
+    // size helpers at the extremes: no signed overflow, no wrapped sizes
+    if (fa_decode_num_splits(INT_MAX, INT_MAX, INT_MAX, 64) < 1) ++failures;
+    if (fa_decode_num_splits(1, 1, INT_MAX, 128) < 1) ++failures;
+    // INT_MAX one-key splits of one head: exactly the grid limit
+    if (fa_decode_workspace_size(1, 1, INT_MAX, 64, INT_MAX) != static_cast<std::size_t>(INT_MAX) * 65 * 4)
+        ++failures;
+    if (fa_decode_workspace_size(2, 1, INT_MAX, 64, INT_MAX) != 0) ++failures;  // twice the limit
+    if (fa_decode_workspace_size(INT_MAX, INT_MAX, INT_MAX, 128, INT_MAX) != 0) ++failures;
+    if (fa_decode_workspace_size(4, 8, 1000, 64, INT_MAX) != static_cast<std::size_t>(4) * 8 * 1000 * 65 * 4)
+        ++failures;
+    if (fa_bwd_workspace_size(INT_MAX, INT_MAX, INT_MAX) != 0) ++failures;
+    if (fa_bwd_workspace_size(1, 1, INT_MAX) != static_cast<std::size_t>(INT_MAX) * 8) ++failures;
 
     if (failures) {
         std::fprintf(stderr, "%d failures\n", failures);

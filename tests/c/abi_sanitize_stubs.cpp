@@ -3,6 +3,7 @@
 // can be linked into a host-only program and run under AddressSanitizer and
 // UndefinedBehaviorSanitizer without a GPU.  Every "launch" succeeds without
 // touching the pointers it is given; a launch with an empty grid is reported.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 
@@ -12,12 +13,16 @@ namespace fa355 {
 
 int fwd_rows_per_block(int) { return 128; }
 
+// The library's rule for the automatic split count, restated so that this
+// host-only program links no device code.
 int decode_auto_splits(int B, int H, int Nkv, int)
 {
-    long long s = (Nkv + 2047) / 2048;
-    const long long bh = static_cast<long long>(B) * H;
-    while (bh * s < 2048 && s * 128 < Nkv) s *= 2;
-    return static_cast<int>(s < 1 ? 1 : s);
+    const long long n_bh = static_cast<long long>(B) * H;
+    if (n_bh < 1 || Nkv < 1) return 1;
+    long long s = std::max<long long>((256 + n_bh - 1) / n_bh, 4);
+    s = std::min<long long>(s, std::max<long long>((2048 + n_bh - 1) / n_bh, 1));
+    s = std::min<long long>(s, (static_cast<long long>(Nkv) + 127) / 128);
+    return static_cast<int>(std::max<long long>(s, 1));
 }
 
 static void expect(bool ok, const char *what)

@@ -94,6 +94,27 @@ def test_caller_stream():
     assert torch.equal(od, od_ref)
 
 
+def test_binding_rejects_misplaced_tensors():
+    # the binding refuses, before any launch, tensors the kernels could not
+    # address: a host LSE for the backward, tensors of the wrong rank
+    q, k, v = _qkv(15, 1, 2, 128, 128, 64)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    say("binding argument checks (no launch)")
+    with pytest.raises(ValueError, match="lse"):
+        fa.bwd(q, k, v, o, q, lse.cpu(), causal=True)
+    with pytest.raises(ValueError, match="dimensions"):
+        fa.fwd(q[0], k[0], v[0])
+    with pytest.raises(ValueError, match="dimensions"):
+        fa.decode(q[:, :, 0].contiguous(), k[0], v[0])
+    # a torch stream object is accepted where the C call takes a stream
+    s = torch.cuda.Stream()
+    o2 = torch.empty_like(o)
+    fa.fa_fwd(q, k, v, o2, None, 1, 2, 128, 128, 64, 1, 1 / np.sqrt(64), fa.FA_F16, s)
+    s.synchronize()
+    assert torch.equal(o2, o)
+
+
 def test_empty_inputs():
     # zero-size tensors (whose data pointers are NULL) through every entry point
     dev = device()
