@@ -11,7 +11,7 @@
 
 namespace fa355 {
 
-int fwd_rows_per_block(int) { return 128; }
+int fwd_rows_per_block(int) { return 64; }
 
 // The library's rule for the automatic split count, restated so that this
 // host-only program links no device code.

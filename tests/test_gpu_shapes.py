@@ -2,7 +2,8 @@
 
 The host picks a workgroup geometry from the grid size:
 - 8 waves (256 query rows) once B*H*ceil(Nq/256) >= 256, 16-bit K only;
-- two 4-wave key groups on 128 rows once B*H*ceil(Nq/128) <= 256 and Nkv > 192;
+- two 4-wave key groups on 128 rows once B*H*ceil(Nq/128) <= 256 and Nkv > 192,
+  or, causal at d = 64 with 16-bit K, two 2-wave key groups on 64 rows;
 - 4 waves (128 rows) otherwise, and always for E4M3 K when the grid is large.
 
 Each case below sits on one side of one of those thresholds (the shape each
@@ -32,6 +33,12 @@ CASES = [
     (1, 128, 256, 192, 128, False, "f16"),  # 4 waves: 192 keys (both)
     (1, 129, 256, 400, 64, True, "bf16"),   # 4 waves: 258 tiles (both)
     (2, 64, 200, 1000, 128, True, "f16"),   # key groups, causal with Nq < Nkv (both)
+    # causal d = 64 small grids: 64-row tiles of two 2-wave key groups (16-bit K)
+    (1, 128, 256, 256, 64, True, "bf16"),   # 64-row key groups: 256 tiles / key groups
+    (1, 129, 256, 256, 64, True, "f16"),    # 4 waves: 258 tiles (both)
+    (1, 3, 300, 1000, 64, True, "f16"),     # 64-row key groups, ragged last tile, Nq < Nkv / key groups
+    (2, 5, 40, 193, 64, True, "bf16"),      # 64-row key groups, one tile whose second wave has 8 rows
+    (1, 8, 130, 192, 64, True, "f16"),      # 4 waves: 192 keys (both)
 ]
 
 
