@@ -15,7 +15,8 @@ bytes (K and V once, q, o and lse).  rank 0 prints one JSON line.
 Separately from the step, the backward (fa_bwd: dQ, dK, dV from O and LSE,
 with dO from the seeded generator) is timed on the prefill workload and
 reported in its own "backward" object, the other two prefill workloads
-(2K d64 fp16 and 16K d128 bf16 causal) in "other_prefill", the FP8 variant (fa_fwd_fp8: Q and K
+(2K d64 fp16 and 16K d128 bf16 causal) in "other_prefill" (also timed as one HIP graph of
+back-to-back calls, since a 2K call is shorter than the host's time to issue it), the FP8 variant (fa_fwd_fp8: Q and K
 rounded to E4M3 for the first product) on the prefill workload in an
 "fp8_forward" object, and decode over a paged cache (fa_decode_paged: the
 decode cache scattered into a shuffled pool of 16-key pages) in a
@@ -357,6 +358,35 @@ def _event_ms(fn, stream, warmup, steps):
     return statistics.fmean(a.elapsed_time(b) for a, b in evs)
 
 
+def _graph_ms(launch, warmup, steps):
+    """Mean time per call when `steps` calls, captured once into a HIP graph,
+    replay back to back: the kernels' own rate, without the host's launch gap
+    between calls (which per-call events include once a call is shorter than
+    the host's time to issue it).  launch(stream_handle) enqueues one call."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(steps):
+            launch(cs)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 SWEEP_PREFILL = (512, 1024, 2048, 4096, 8192, 16384, 32768)
 SWEEP_DECODE = (1024, 4096, 16384, 32768)
 
@@ -525,12 +555,21 @@ def time_other_prefill(fa, fi, names, dev, stream, warmup, steps):
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
         code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
-        ms = _event_ms(lambda: fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal, w.scale, code, sp),
-                       stream, warmup, steps)
+        call = lambda s: fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal, w.scale, code, s)
+        ms = _event_ms(lambda: call(sp), stream, warmup, steps)
+        o_eager, lse_eager = o.clone(), lse.clone()
+        ms_graph = _graph_ms(call, warmup, steps)
+        same = bool(torch.equal(o, o_eager) and torch.equal(lse, lse_eager))
         flops = metric_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
-        tf = flops / (ms * 1e-3) / 1e12
+        tf, tf_graph = flops / (ms * 1e-3) / 1e12, flops / (ms_graph * 1e-3) / 1e12
         res.append({"workload": name, "B": w.B, "H": w.H, "N": w.Nq, "d": w.d, "dtype": w.dtype, "causal": w.causal,
-                    "ms_mean": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4)})
+                    "ms_mean": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_MFMA_F16_TFLOPS, 4),
+                    "ms_graph": round(ms_graph, 4), "TFLOP/s_graph": round(tf_graph, 2),
+                    "frac_of_mfma_peak_graph": round(tf_graph / PEAK_MFMA_F16_TFLOPS, 4),
+                    "graph_output_equals_eager": same,
+                    "note": "ms_mean: each call between its own HIP events (includes the host's launch gap for "
+                            "short calls); ms_graph: the same calls captured once into a HIP graph and replayed "
+                            "back to back"})
         q = k = v = o = lse = None
     return res
 

@@ -115,6 +115,54 @@ def test_binding_rejects_misplaced_tensors():
     assert torch.equal(o2, o)
 
 
+def test_graph_capture_replays():
+    # the entry points enqueue kernels only (no allocation, no memset, no
+    # synchronisation), so a caller can capture them into a HIP graph; every
+    # replay, with eager work of the program between replays, gives the bits
+    # of the eager calls
+    B, H, N, d = 1, 4, 300, 64
+    q, k, v = _qkv(16, B, H, N, N, d)
+    dev = q.device
+    code = fa.FA_F16
+    scale = 1 / np.sqrt(d)
+    o, lse = torch.empty_like(q), torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    qd = q[:, :, -1].contiguous()
+    od, lsed = torch.empty_like(qd), torch.empty(B, H, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_decode_workspace_size(B, H, N, d, 0), dtype=torch.uint8, device=dev)
+    g3 = [torch.empty_like(q) for _ in range(3)]
+    bws = torch.empty(fa.fa_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
+
+    def calls(s):
+        fa.fa_fwd(q, k, v, o, lse, B, H, N, N, d, 1, scale, code, s)
+        fa.fa_decode(qd, k, v, od, lsed, B, H, N, d, scale, code, 0, ws, ws.numel(), s)
+        fa.fa_bwd(q, k, v, o, q, lse, g3[0], g3[1], g3[2], B, H, N, N, d, 1, scale, code, bws, bws.numel(), s)
+
+    outs = (o, lse, od, lsed, *g3)
+    say("eager calls, then capture into a graph")
+    calls(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(torch.cuda.current_stream().cuda_stream)
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        other, _ = fa.fwd(q, k, v, causal=False)  # eager work between replays
+        torch.cuda.synchronize()
+        say(f"graph replay {r}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref)), f"replay {r}"
+        assert not torch.isnan(other).any()
+
+
 def test_empty_inputs():
     # zero-size tensors (whose data pointers are NULL) through every entry point
     dev = device()
