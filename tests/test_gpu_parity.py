@@ -266,6 +266,38 @@ def test_full_size_prefill_sampled(name):
         check(o, lse, o_ref, lse_ref, w.dtype, f"{name} head {bh} rows {len(rows)}")
 
 
+WIDE_RECT = [
+    # B, H, Nq, Nkv, d, dtype: causal with Nq < Nkv (bottom-right) on grids that
+    # select the 8-wave shape for 16-bit K and the 4-wave shape for E4M3 K
+    (1, 64, 1500, 5000, 128, "f16"),
+    (1, 128, 777, 3333, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_RECT, ids=lambda c: "B{}H{}q{}k{}d{}{}".format(*c))
+def test_wide_causal_rectangular_sampled(case):
+    B, H, Nq, Nkv, d, dtype = case
+    rng = np.random.default_rng(Nq * Nkv)
+    q = rand_bits(rng, (B, H, Nq, d), dtype)
+    k = rand_bits(rng, (B, H, Nkv, d), dtype)
+    v = rand_bits(rng, (B, H, Nkv, d), dtype)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    tq, tk, tv = upload(q, dtype), upload(k, dtype), upload(v, dtype)
+    say(f"fa_fwd and fa_fwd_fp8 causal rectangular {case}")
+    o, lse = fa.fwd(tq, tk, tv, causal=True, scale=scale, out_dtype=torch.float32)
+    o8, lse8 = fa.fwd_fp8(tq, tk, tv, causal=True, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o, lse, o8, lse8 = to_np(o), to_np(lse), to_np(o8), to_np(lse8)
+    for bh in sorted({0, B * H // 2, B * H - 1}):
+        b, h = divmod(bh, H)
+        rows = _sample_rows(Nq, rng)
+        o_ref, lse_ref = oracle.attention_rows(q[b, h], k[b, h], v[b, h], rows, causal=True, scale=scale, dtype=dtype)
+        check(o[b, h][rows], lse[b, h][rows], o_ref, lse_ref, dtype, f"fwd {case} head {bh}")
+        o_ref, lse_ref = oracle.attention_fp8qk_rows(q[b, h], k[b, h], v[b, h], rows, causal=True, scale=scale,
+                                                     dtype=dtype)
+        check(o8[b, h][rows], lse8[b, h][rows], o_ref, lse_ref, dtype, f"fwd_fp8 {case} head {bh}")
+
+
 def test_full_size_decode_sampled():
     w = fi.WORKLOADS["decode_32k_d128"]
     say("generate decode_32k_d128")
