@@ -28,7 +28,9 @@
 // Pass 2 (combine kernel): per head, the partial results are merged exactly
 // by their log-sum-exp values, the two-block merge of "FlashAttention 1-2-3
 // ...", section "The Math Behind the Online Softmax Trick", applied to all
-// chunks at once: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
+// chunks at once: O = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).  With
+// one split per head the split kernel writes O and LSE itself and pass 2 is
+// not launched.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -43,8 +45,10 @@ constexpr int kDecUnroll = 8;  // key rows in flight per lane group per iteratio
 
 struct SplitParams {
     const void *q, *k, *v;
+    void *o;     // written directly when splits == 1
+    float *lse;  // may be null
     float *ws_o, *ws_lse;
-    int Nkv, chunk, splits;
+    int Nkv, chunk, splits, out_f32;
     float scale_log2;
     // paged cache only
     const int *block_table;  // [B][max_pages] page indices
@@ -220,10 +224,23 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_split_kernel(SplitParam
             L += s_l[G] * wgt;
             o += s_acc[G][tid] * wgt;
         }
-        const size_t slot = static_cast<size_t>(bh) * p.splits + split;
         // an empty chunk (paged: past the sequence's end) contributes weight 0
-        p.ws_o[slot * D + tid] = L > 0.f ? o / L : 0.f;
-        if (tid == 0) p.ws_lse[slot] = L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;
+        const float o_n = L > 0.f ? o / L : 0.f;
+        const float lse2 = L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;
+        if (p.splits == 1) {
+            // one chunk per head is the whole cache: its normalised output and
+            // LSE are the result (the merge of one partial has weight 2^0 = 1)
+            const size_t i = static_cast<size_t>(bh) * D + tid;
+            if (p.out_f32)
+                static_cast<float *>(p.o)[i] = o_n;
+            else
+                static_cast<T *>(p.o)[i] = static_cast<T>(o_n);
+            if (tid == 0 && p.lse) p.lse[bh] = lse2 * kLn2;
+        } else {
+            const size_t slot = static_cast<size_t>(bh) * p.splits + split;
+            p.ws_o[slot * D + tid] = o_n;
+            if (tid == 0) p.ws_lse[slot] = lse2;
+        }
     }
 }
 
@@ -318,6 +335,9 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream)
     sp.q = a.q;
     sp.k = a.k;
     sp.v = a.v;
+    sp.o = a.o;
+    sp.lse = a.lse;
+    sp.out_f32 = a.out_f32 ? 1 : 0;
     sp.ws_o = a.ws_o;
     sp.ws_lse = a.ws_lse;
     sp.Nkv = a.Nkv;
@@ -344,7 +364,7 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream)
     const dim3 grid1(static_cast<unsigned>(static_cast<long long>(n_bh) * a.splits));
     hipLaunchKernelGGL((decode_split_kernel<D, T, PAGED>), grid1, dim3(64 * kDecWaves), 0, stream, sp);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || a.splits == 1) return err;
 
     CombineParams cp;
     cp.ws_o = a.ws_o;

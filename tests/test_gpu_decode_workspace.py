@@ -9,7 +9,9 @@ here check that
   and the same bits every time;
 - split counts around the merge's unrolled loop (four rows in flight per
   group of threads, then a tail) merge every chunk exactly once;
-- many heads merged at once stay independent and deterministic.
+- many heads merged at once stay independent and deterministic;
+- with one split per head (chosen automatically once B*H fills the chip)
+  the split kernel's own result is the oracle's.
 """
 import numpy as np
 import pytest
@@ -126,3 +128,20 @@ def test_many_heads_merge_at_once():
     o16, _ = fa.decode(tq[:, :, 0].contiguous(), tk, tv, scale=1 / np.sqrt(d), num_splits=4)
     torch.cuda.synchronize()
     assert np.array_equal(fi.torch_to_bits(o16.cpu()), fi.f32_to_bits(to_np(outs[0][0]).astype(np.float32), dtype))
+
+
+def test_automatic_single_split():
+    # 2048 heads fill the chip with one workgroup each: the automatic split
+    # count is 1, and the split kernel writes O and LSE itself
+    B, H, Nkv, d, dtype = 32, 64, 300, 64, "f16"
+    assert fa.fa_decode_num_splits(B, H, Nkv, d) == 1
+    q, k, v = _case(12, B, H, Nkv, d, dtype)
+    tq, tk, tv = upload(q, dtype), upload(k, dtype), upload(v, dtype)
+    say("fa_decode 32 x 64 heads x 300 keys, automatic split count (1)")
+    o, lse = fa.decode(tq[:, :, 0].contiguous(), tk, tv, scale=1 / np.sqrt(d), out_dtype=torch.float32)
+    o16, lse16 = fa.decode(tq[:, :, 0].contiguous(), tk, tv, scale=1 / np.sqrt(d))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, causal=False, scale=float(np.float32(1 / np.sqrt(d))), dtype=dtype)
+    check(to_np(o)[:, :, None], to_np(lse)[..., None], o_ref, lse_ref, dtype, "decode, one split per head")
+    assert torch.equal(lse16, lse)
+    assert np.array_equal(fi.torch_to_bits(o16.cpu()), fi.f32_to_bits(to_np(o).astype(np.float32), dtype))
