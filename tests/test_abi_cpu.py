@@ -232,7 +232,7 @@ def test_decode_sizes():
     assert dec(B=0, q=None, k=None, v=None, o=None, lse=None, ws=None, ws_bytes=0)[0] == fa.FA_OK
 
 
-def test_last_error_is_per_thread():
+def test_last_error_is_empty_in_a_new_thread():
     import threading
     fwd(d=96)
     seen = {}
@@ -307,7 +307,7 @@ def test_abi_from_c(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
 
 
-def test_last_error_is_per_thread():
+def test_last_error_is_per_thread_under_contention():
     # each thread sees the message of its own last failing call
     import threading
     results = {}
