@@ -31,6 +31,7 @@ host's cores; it is a reference point, not the target.
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bwd] [--no-other] [--no-fp8] [--no-paged]
     python bench.py --sweep [--steps K] [--warmup W]   # fused vs unfused over sequence length
     python bench.py --map [--steps K] [--warmup W]     # fused kernels over N, d, mask, type
+    python bench.py --data-probe [--steps K] [--warmup W]  # fa_fwd on workload, zero and constant inputs
 """
 from __future__ import annotations
 
@@ -539,6 +540,56 @@ def run_map(warmup, steps):
     return out
 
 
+DATA_PROBE = ("prefill_8k_d128", "prefill_16k_d128_bf16")
+
+
+def run_data_probe(warmup, steps, rounds=6):
+    """fa_fwd on the two long prefill workloads with three kinds of input of
+    the same shapes: the seeded workload inputs, all zeros, and constants
+    (q = 0.5, k = 0.25, v = 1).  The kernel runs the same instructions on all
+    three (the rescale branch aside, which the workload inputs rarely take), so
+    a difference in time is the data's switching activity in the datapaths,
+    i.e. the chip's power limit.  The kinds are timed in interleaved rounds
+    and the median round is reported.  Timing only: no parity claim."""
+    import torch
+
+    import exact_io_aware_65_amd as fa
+    import fa_inputs as fi
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    out = []
+    for name in DATA_PROBE:
+        w = fi.WORKLOADS[name]
+        x = fi.make_inputs(w)
+        q, k, v = (fi.bits_to_torch(x[t], w.dtype).to(dev) for t in "qkv")
+        x = None
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+        kinds = {"workload": (q, k, v),
+                 "zeros": tuple(torch.zeros_like(t) for t in (q, k, v)),
+                 "constant": (torch.full_like(q, 0.5), torch.full_like(k, 0.25), torch.full_like(v, 1.0))}
+        times = {kind: [] for kind in kinds}
+        for r in range(rounds):
+            for kind in (list(kinds) if r % 2 == 0 else list(kinds)[::-1]):
+                a, b, c = kinds[kind]
+                times[kind].append(_event_ms(
+                    lambda: fa.fa_fwd(a, b, c, o, lse, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal, w.scale, code, sp),
+                    stream, warmup, steps))
+        flops = metric_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
+        base = statistics.median(times["workload"])
+        for kind, ts in times.items():
+            ms = statistics.median(ts)
+            out.append({"workload": name, "inputs": kind, "ms": round(ms, 4),
+                        "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "speed_vs_workload_inputs": round(base / ms, 3),
+                        "rounds_ms": [round(t, 4) for t in ts]})
+            print(f"[data-probe] {name} {kind}: {flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        q = k = v = o = lse = kinds = None
+        torch.cuda.empty_cache()
+    return out
+
+
 OTHER_PREFILL = ("prefill_2k_d64", "prefill_16k_d128_bf16")
 
 
@@ -646,6 +697,8 @@ def main():
                     help="only run the speed-vs-length sweep of the fused kernels against the unfused baseline")
     ap.add_argument("--map", action="store_true",
                     help="only run the speed map of the fused kernels over sequence length, head dim, mask and type")
+    ap.add_argument("--data-probe", action="store_true",
+                    help="only time fa_fwd on the long prefill workloads with workload, all-zero and constant inputs")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the timing of the other prefill workloads (2K d64, 16K d128 bf16)")
     ap.add_argument("--no-fp8", action="store_true",
@@ -667,6 +720,13 @@ def main():
         res = run_map(max(1, args.warmup), max(1, args.steps))
         print(json.dumps({"metric": "fused kernel speed over shapes", "unit": "TFLOP/s, GB/s",
                           "higher_is_better": True, "data": "synthetic", "map": res}), flush=True)
+        return
+    if args.data_probe:
+        if args.gpus != 1:
+            sys.exit("bench.py --data-probe measures one GPU only")
+        res = run_data_probe(max(1, args.warmup), max(1, args.steps))
+        print(json.dumps({"metric": "fa_fwd speed by input data at fixed shapes", "unit": "TFLOP/s",
+                          "higher_is_better": True, "data": "synthetic", "probe": res}), flush=True)
         return
     if args.gpus != 1:
         if int(os.environ.get("RANK", "0")) == 0:
