@@ -546,7 +546,8 @@ DATA_PROBE = ("prefill_8k_d128", "prefill_16k_d128_bf16")
 def run_data_probe(warmup, steps, rounds=6):
     """fa_fwd on the two long prefill workloads with three kinds of input of
     the same shapes: the seeded workload inputs, all zeros, and constants
-    (q = 0.5, k = 0.25, v = 1).  The kernel runs the same instructions on all
+    (q = 0.5, k = 0.25, v = 1); then, as a control, fa_decode on the decode
+    workload's shapes with normal, zero and constant inputs.  The kernel runs the same instructions on all
     three (the rescale branch aside, which the workload inputs rarely take), so
     a difference in time is the data's switching activity in the datapaths,
     i.e. the chip's power limit.  The kinds are timed in interleaved rounds
@@ -587,6 +588,33 @@ def run_data_probe(warmup, steps, rounds=6):
             print(f"[data-probe] {name} {kind}: {flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s", file=sys.stderr, flush=True)
         q = k = v = o = lse = kinds = None
         torch.cuda.empty_cache()
+    # Control: decode streams its cache from HBM, so its speed should not
+    # depend on the data.  Normal inputs are drawn on the device here.
+    w = fi.WORKLOADS[DECODE]
+    q = fi.device_normals((w.B, w.H, w.d), w.dtype, 300, dev)
+    k, v = (fi.device_normals((w.B, w.H, w.Nkv, w.d), w.dtype, 301 + t, dev) for t in range(2))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    nbytes = fa.fa_decode_workspace_size(w.B, w.H, w.Nkv, w.d, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dcode = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+    kinds = {"normal": (q, k, v)}
+    kinds["zeros"] = tuple(torch.zeros_like(t) for t in (q, k, v))
+    kinds["constant"] = (torch.full_like(q, 0.5), torch.full_like(k, 0.25), torch.full_like(v, 1.0))
+    times = {kind: [] for kind in kinds}
+    for r in range(rounds):
+        for kind in (list(kinds) if r % 2 == 0 else list(kinds)[::-1]):
+            a, b, c = kinds[kind]
+            times[kind].append(_event_ms(
+                lambda: fa.fa_decode(a, b, c, o, lse, w.B, w.H, w.Nkv, w.d, w.scale, dcode, 0, ws, nbytes, sp),
+                stream, warmup, steps))
+    nb = algorithmic_bytes(w.B, w.H, 1, w.Nkv, w.d)
+    base = statistics.median(times["normal"])
+    for kind, ts in times.items():
+        ms = statistics.median(ts)
+        out.append({"workload": DECODE, "inputs": kind, "ms": round(ms, 4), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                    "speed_vs_workload_inputs": round(base / ms, 3), "rounds_ms": [round(t, 4) for t in ts]})
+        print(f"[data-probe] {DECODE} {kind}: {nb / (ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
     return out
 
 
@@ -698,7 +726,7 @@ def main():
     ap.add_argument("--map", action="store_true",
                     help="only run the speed map of the fused kernels over sequence length, head dim, mask and type")
     ap.add_argument("--data-probe", action="store_true",
-                    help="only time fa_fwd on the long prefill workloads with workload, all-zero and constant inputs")
+                    help="only time fa_fwd on the long prefill workloads (and fa_decode as a control) with workload, all-zero and constant inputs")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the timing of the other prefill workloads (2K d64, 16K d128 bf16)")
     ap.add_argument("--no-fp8", action="store_true",
