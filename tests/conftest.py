@@ -13,3 +13,9 @@ if TESTS not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def pytest_report_header(config):
+    # which build of the library the binding loads (FA355_LIBRARY selects another one)
+    from exact_io_aware_65_amd._binding import LIBRARY
+    return f"libfa355 under test: {LIBRARY}"
