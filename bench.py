@@ -546,7 +546,8 @@ DATA_PROBE = ("prefill_8k_d128", "prefill_16k_d128_bf16")
 def run_data_probe(warmup, steps, rounds=6):
     """fa_fwd on the two long prefill workloads with three kinds of input of
     the same shapes: the seeded workload inputs, all zeros, and constants
-    (q = 0.5, k = 0.25, v = 1); then, as a control, fa_decode on the decode
+    (q = 0.5, k = 0.25, v = 1), and fa_bwd on the first of them with the same
+    kinds of data; then, as a control, fa_decode on the decode
     workload's shapes with normal, zero and constant inputs.  The kernel runs the same instructions on all
     three (the rescale branch aside, which the workload inputs rarely take), so
     a difference in time is the data's switching activity in the datapaths,
@@ -586,6 +587,37 @@ def run_data_probe(warmup, steps, rounds=6):
                         "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "speed_vs_workload_inputs": round(base / ms, 3),
                         "rounds_ms": [round(t, 4) for t in ts]})
             print(f"[data-probe] {name} {kind}: {flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        if name == PREFILL:
+            # the backward on the same kinds of data: O and LSE from each kind's
+            # forward, dO normal / zero / constant like the inputs
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            bws = torch.empty(max(fa.fa_bwd_workspace_size(w.B, w.H, w.Nq), 16), dtype=torch.uint8, device=dev)
+            grads = {"workload": fi.device_normals(tuple(q.shape), w.dtype, 400, dev),
+                     "zeros": torch.zeros_like(q), "constant": torch.full_like(q, 1.0)}
+            saved = {}
+            for kind, (a, b, c) in kinds.items():
+                ok, lk = torch.empty_like(q), torch.empty_like(lse)
+                fa.fa_fwd(a, b, c, ok, lk, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal, w.scale, code, sp)
+                saved[kind] = (ok, lk)
+            btimes = {kind: [] for kind in kinds}
+            for r in range(rounds):
+                for kind in (list(kinds) if r % 2 == 0 else list(kinds)[::-1]):
+                    a, b, c = kinds[kind]
+                    ok, lk = saved[kind]
+                    do = grads[kind]
+                    btimes[kind].append(_event_ms(
+                        lambda: fa.fa_bwd(a, b, c, ok, do, lk, dq, dk, dv, w.B, w.H, w.Nq, w.Nkv, w.d, w.causal,
+                                          w.scale, code, bws, bws.numel(), sp), stream, warmup, steps))
+            bflops = backward_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
+            bbase = statistics.median(btimes["workload"])
+            for kind, ts in btimes.items():
+                ms = statistics.median(ts)
+                out.append({"workload": name, "kernel": "fa_bwd", "inputs": kind, "ms": round(ms, 4),
+                            "TFLOP/s": round(bflops / (ms * 1e-3) / 1e12, 1),
+                            "speed_vs_workload_inputs": round(bbase / ms, 3), "rounds_ms": [round(t, 4) for t in ts]})
+                print(f"[data-probe] {name} fa_bwd {kind}: {bflops / (ms * 1e-3) / 1e12:.0f} TFLOP/s", file=sys.stderr,
+                      flush=True)
+            dq = dk = dv = bws = grads = saved = None
         q = k = v = o = lse = kinds = None
         torch.cuda.empty_cache()
     # Control: decode streams its cache from HBM, so its speed should not
