@@ -16,6 +16,8 @@ and, for the backward with dL/dO = dO, the chain rule through that definition:
     dV = P^T dO, dP = dO V^T, D = rowsum(P * dP), dS = P * (dP - D),
     dQ = scale * dS K, dK = scale * dS^T Q
 
+(with D optionally formed as rowsum(dO * O) from a given forward output O,
+the O a training step hands its backward)
 decode over a paged cache (the dense attention over each sequence's keys,
 gathered through a block table), and the FP8 variant (Q and K rounded to
 E4M3 -- nearest even, saturating at 448 -- before the first product).
@@ -71,10 +73,10 @@ class Oracle:
                                                  ctypes.c_double, ctypes.POINTER(_i64), _i64,
                                                  _dp, _dp]
         lib.fa_oracle_attention_rows.restype = ctypes.c_int
-        lib.fa_oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64,
+        lib.fa_oracle_attention_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64,
                                                 _i64, _i64, ctypes.c_int, ctypes.c_double]
         lib.fa_oracle_attention_bwd.restype = ctypes.c_int
-        lib.fa_oracle_attention_bwd_sampled.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int,
+        lib.fa_oracle_attention_bwd_sampled.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int,
                                                         ctypes.c_double, ctypes.POINTER(_i64), _i64,
                                                         ctypes.POINTER(_i64), _i64, _dp, _dp, _dp]
         lib.fa_oracle_attention_bwd_sampled.restype = ctypes.c_int
@@ -148,20 +150,28 @@ class Oracle:
             raise ValueError(f"oracle rejected the call (rc={rc})")
         return o, lse
 
-    def attention_bwd(self, q, k, v, dout, *, causal: bool, scale: float, dtype=None):
-        """(dQ, dK, dV) in float64 for dL/dO = dout; shapes as for attention()."""
+    def attention_bwd(self, q, k, v, dout, *, causal: bool, scale: float, dtype=None, o_for_d=None):
+        """(dQ, dK, dV) in float64 for dL/dO = dout; shapes as for attention().
+
+        o_for_d (like q; bits when dtype is given): the forward output the
+        backward is handed, from which D_i = sum_c dout_ic o_ic is formed;
+        None forms D from P itself (the same value for the exact O)."""
         q, k, v, dout = (self._as_f64(t, dtype) for t in (q, k, v, dout))
+        od = None if o_for_d is None else self._as_f64(o_for_d, dtype)
         squeeze = q.ndim == 2
         if squeeze:
             q, k, v, dout = q[None, None], k[None, None], v[None, None], dout[None, None]
+            od = None if od is None else od[None, None]
         B, H, Nq, d = q.shape
         Nkv = k.shape[2]
-        if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d) or dout.shape != q.shape:
+        if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d) or dout.shape != q.shape or \
+                (od is not None and od.shape != q.shape):
             raise ValueError("shape mismatch")
         dq = np.empty_like(q)
         dk = np.empty_like(k)
         dv = np.empty_like(v)
-        rc = self.lib.fa_oracle_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+        rc = self.lib.fa_oracle_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                              None if od is None else _ptr(od), _ptr(dq), _ptr(dk),
                                               _ptr(dv), B, H, Nq, Nkv, d, int(bool(causal)), float(scale))
         if rc:
             raise ValueError(f"oracle rejected the call (rc={rc})")
@@ -169,9 +179,14 @@ class Oracle:
             return dq[0, 0], dk[0, 0], dv[0, 0]
         return dq, dk, dv
 
-    def attention_bwd_sampled(self, q, k, v, dout, qrows, kcols, *, causal: bool, scale: float, dtype=None):
-        """One head: dQ at query rows qrows [n,d], dK and dV at key rows kcols [m,d]."""
+    def attention_bwd_sampled(self, q, k, v, dout, qrows, kcols, *, causal: bool, scale: float, dtype=None,
+                              o_for_d=None):
+        """One head: dQ at query rows qrows [n,d], dK and dV at key rows kcols [m,d]; o_for_d as for
+        attention_bwd ([Nq,d])."""
         q, k, v, dout = (self._as_f64(t, dtype) for t in (q, k, v, dout))
+        od = None if o_for_d is None else self._as_f64(o_for_d, dtype)
+        if od is not None and od.shape != q.shape:
+            raise ValueError("shape mismatch")
         qrows = np.ascontiguousarray(qrows, dtype=np.int64)
         kcols = np.ascontiguousarray(kcols, dtype=np.int64)
         Nq, d = q.shape
@@ -179,7 +194,8 @@ class Oracle:
         dq = np.empty((qrows.size, d))
         dk = np.empty((kcols.size, d))
         dv = np.empty((kcols.size, d))
-        rc = self.lib.fa_oracle_attention_bwd_sampled(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), Nq, Nkv, d,
+        rc = self.lib.fa_oracle_attention_bwd_sampled(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                                      None if od is None else _ptr(od), Nq, Nkv, d,
                                                       int(bool(causal)), float(scale), _ptr(qrows, _i64),
                                                       qrows.size, _ptr(kcols, _i64), kcols.size, _ptr(dq),
                                                       _ptr(dk), _ptr(dv))
@@ -290,12 +306,13 @@ def attention_rows(q, k, v, rows, *, causal, scale, dtype=None):
     return default().attention_rows(q, k, v, rows, causal=causal, scale=scale, dtype=dtype)
 
 
-def attention_bwd(q, k, v, dout, *, causal, scale, dtype=None):
-    return default().attention_bwd(q, k, v, dout, causal=causal, scale=scale, dtype=dtype)
+def attention_bwd(q, k, v, dout, *, causal, scale, dtype=None, o_for_d=None):
+    return default().attention_bwd(q, k, v, dout, causal=causal, scale=scale, dtype=dtype, o_for_d=o_for_d)
 
 
-def attention_bwd_sampled(q, k, v, dout, qrows, kcols, *, causal, scale, dtype=None):
-    return default().attention_bwd_sampled(q, k, v, dout, qrows, kcols, causal=causal, scale=scale, dtype=dtype)
+def attention_bwd_sampled(q, k, v, dout, qrows, kcols, *, causal, scale, dtype=None, o_for_d=None):
+    return default().attention_bwd_sampled(q, k, v, dout, qrows, kcols, causal=causal, scale=scale, dtype=dtype,
+                                           o_for_d=o_for_d)
 
 
 def paged_decode(q, k_pages, v_pages, block_table, seq_lens, *, scale, layout="hnd", dtype=None):

@@ -242,15 +242,24 @@ int fa_oracle_attention_rows(const double *q, const double *k, const double *v, 
  *   dV[j][c] = sum_i P[i][j] * dO[i][c]
  *   dP[i][j] = sum_c dO[i][c] * v[j][c]
  *   D_i      = sum_j P[i][j] * dP[i][j]       (softmax Jacobian: row-wise)
+ *            = sum_c dO[i][c] * O[i][c]       (the same number, as O = P v)
  *   dS[i][j] = P[i][j] * (dP[i][j] - D_i)
  *   dQ[i][c] = scale * sum_j dS[i][j] * k[j][c]
  *   dK[j][c] = scale * sum_i dS[i][j] * q[i][c]
  *
  * Invisible keys have P = 0 and so dS = 0.  P is recomputed from q and k here
  * (the oracle stores nothing between calls).
+ *
+ * The backward of a training step is handed the forward's output O as the
+ * caller holds it (rounded to the 16-bit input type), and forms D from it
+ * ("Flash Attention -- Module 12.3", section "Training": the backward works
+ * from what the forward kept).  Reading taken here: when oD is given, D_i is
+ * the second form above evaluated on that O, D_i = sum_c dO[i][c] * oD[i][c];
+ * when oD is NULL, D_i is the first form, from P itself.  With oD = P v
+ * exactly the two agree.
  */
 static int head_attention_bwd(const double *q, const double *k, const double *v, const double *dO,
-                              double *dq, double *dk, double *dv, int64_t Nq, int64_t Nkv,
+                              const double *oD, double *dq, double *dk, double *dv, int64_t Nq, int64_t Nkv,
                               int64_t d, int causal, double scale)
 {
     double *P = (double *)malloc((size_t)Nq * (size_t)Nkv * sizeof(double));
@@ -272,6 +281,11 @@ static int head_attention_bwd(const double *q, const double *k, const double *v,
                 dp += dO[i * d + c] * v[j * d + c];
             ds_row[j] = dp;
             Di += p_row[j] * dp;
+        }
+        if (oD) {
+            Di = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                Di += dO[i * d + c] * oD[i * d + c];
         }
         for (int64_t j = 0; j < Nkv; ++j)
             ds_row[j] = p_row[j] * (ds_row[j] - Di);
@@ -300,19 +314,20 @@ static int head_attention_bwd(const double *q, const double *k, const double *v,
 }
 
 /*
- * Gradients over [B][H][N][d] inputs: dO like o, dq like q, dk and dv like k.
+ * Gradients over [B][H][N][d] inputs: dO like o, dq like q, dk and dv like k;
+ * oD (like o, or NULL) is the forward output D is formed from (see above).
  * Returns 0, -1 for an invalid shape, -2 if a score matrix cannot be allocated.
  */
 int fa_oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dO,
-                            double *dq, double *dk, double *dv, int64_t B, int64_t H, int64_t Nq,
-                            int64_t Nkv, int64_t d, int causal, double scale)
+                            const double *oD, double *dq, double *dk, double *dv, int64_t B, int64_t H,
+                            int64_t Nq, int64_t Nkv, int64_t d, int causal, double scale)
 {
     if (B < 0 || H < 0 || check_shape(Nq, Nkv, d, causal))
         return -1;
     for (int64_t bh = 0; bh < B * H; ++bh) {
         int rc = head_attention_bwd(q + bh * Nq * d, k + bh * Nkv * d, v + bh * Nkv * d,
-                                    dO + bh * Nq * d, dq + bh * Nq * d, dk + bh * Nkv * d,
-                                    dv + bh * Nkv * d, Nq, Nkv, d, causal, scale);
+                                    dO + bh * Nq * d, oD ? oD + bh * Nq * d : NULL, dq + bh * Nq * d,
+                                    dk + bh * Nkv * d, dv + bh * Nkv * d, Nq, Nkv, d, causal, scale);
         if (rc)
             return rc;
     }
@@ -327,11 +342,11 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v, c
  * column of P and dS, each entry recomputed from LSE_i and D_i as
  * P_ij = exp(S_ij - LSE_i), dS_ij = P_ij * (dP_ij - D_i).
  * q, dO: [Nq][d]; k, v: [Nkv][d]; qrows / kcols list indices; dq gets
- * [nq][d], dk and dv [nk][d].  Returns 0, -1 for bad arguments, -2 if out of
- * memory.
+ * [nq][d], dk and dv [nk][d]; oD ([Nq][d] or NULL) as for the full entry.
+ * Returns 0, -1 for bad arguments, -2 if out of memory.
  */
 int fa_oracle_attention_bwd_sampled(const double *q, const double *k, const double *v, const double *dO,
-                                    int64_t Nq, int64_t Nkv, int64_t d, int causal, double scale,
+                                    const double *oD, int64_t Nq, int64_t Nkv, int64_t d, int causal, double scale,
                                     const int64_t *qrows, int64_t nq, const int64_t *kcols, int64_t nk,
                                     double *dq, double *dk, double *dv)
 {
@@ -369,6 +384,11 @@ int fa_oracle_attention_bwd_sampled(const double *q, const double *k, const doub
                 dp += v[j * d + c] * dO[i * d + c];
             dp_row[j] = dp;
             Di += p_row[j] * dp;
+        }
+        if (oD) {
+            Di = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                Di += dO[i * d + c] * oD[i * d + c];
         }
         Dv[i] = Di;
         free(row);

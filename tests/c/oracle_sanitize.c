@@ -15,12 +15,13 @@ int fa_oracle_attention(const double *q, const double *k, const double *v, doubl
                         int64_t H, int64_t Nq, int64_t Nkv, int64_t d, int causal, double scale);
 int fa_oracle_attention_rows(const double *q, const double *k, const double *v, int64_t Nq, int64_t Nkv, int64_t d,
                              int causal, double scale, const int64_t *rows, int64_t nrows, double *o, double *lse);
-int fa_oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dO, double *dq,
-                            double *dk, double *dv, int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d,
-                            int causal, double scale);
-int fa_oracle_attention_bwd_sampled(const double *q, const double *k, const double *v, const double *dO, int64_t Nq,
-                                    int64_t Nkv, int64_t d, int causal, double scale, const int64_t *qrows,
-                                    int64_t nq, const int64_t *kcols, int64_t nk, double *dq, double *dk, double *dv);
+int fa_oracle_attention_bwd(const double *q, const double *k, const double *v, const double *dO, const double *oD,
+                            double *dq, double *dk, double *dv, int64_t B, int64_t H, int64_t Nq, int64_t Nkv,
+                            int64_t d, int causal, double scale);
+int fa_oracle_attention_bwd_sampled(const double *q, const double *k, const double *v, const double *dO,
+                                    const double *oD, int64_t Nq, int64_t Nkv, int64_t d, int causal, double scale,
+                                    const int64_t *qrows, int64_t nq, const int64_t *kcols, int64_t nk, double *dq,
+                                    double *dk, double *dv);
 int fa_oracle_paged_decode(const double *q, const double *kpool, const double *vpool, const int32_t *table,
                            const int32_t *lens, double *o, double *lse, int64_t B, int64_t H, int64_t num_pages,
                            int64_t page_size, int64_t max_pages, int64_t d, int layout, double scale);
@@ -75,13 +76,18 @@ int main(void)
         CHECK(finite_all(o, nq) && finite_all(lse, B * H * Nq));
         CHECK(fa_oracle_attention_fp8qk(q, k, v, o, lse, B, H, Nq, Nkv, d, causal, 0.3) == 0);
         CHECK(finite_all(o, nq) && finite_all(lse, B * H * Nq));
-        CHECK(fa_oracle_attention_bwd(q, k, v, dO, dq, dk, dv, B, H, Nq, Nkv, d, causal, 0.3) == 0);
+        CHECK(fa_oracle_attention_bwd(q, k, v, dO, NULL, dq, dk, dv, B, H, Nq, Nkv, d, causal, 0.3) == 0);
+        CHECK(finite_all(dq, nq) && finite_all(dk, nk) && finite_all(dv, nk));
+        CHECK(fa_oracle_attention_bwd(q, k, v, dO, o, dq, dk, dv, B, H, Nq, Nkv, d, causal, 0.3) == 0);
         CHECK(finite_all(dq, nq) && finite_all(dk, nk) && finite_all(dv, nk));
         const int64_t rows[3] = {0, 18, Nq - 1}, cols[3] = {0, 1, Nkv - 1};
         double ro[3 * 16], rl[3], sdq[3 * 16], sdk[3 * 16], sdv[3 * 16];
         CHECK(fa_oracle_attention_rows(q, k, v, Nq, Nkv, d, causal, 0.3, rows, 3, ro, rl) == 0);
         CHECK(finite_all(ro, 3 * 16) && finite_all(rl, 3));
-        CHECK(fa_oracle_attention_bwd_sampled(q, k, v, dO, Nq, Nkv, d, causal, 0.3, rows, 3, cols, 3, sdq, sdk,
+        CHECK(fa_oracle_attention_bwd_sampled(q, k, v, dO, NULL, Nq, Nkv, d, causal, 0.3, rows, 3, cols, 3, sdq,
+                                              sdk, sdv) == 0);
+        CHECK(finite_all(sdq, 3 * 16) && finite_all(sdk, 3 * 16) && finite_all(sdv, 3 * 16));
+        CHECK(fa_oracle_attention_bwd_sampled(q, k, v, dO, o, Nq, Nkv, d, causal, 0.3, rows, 3, cols, 3, sdq, sdk,
                                               sdv) == 0);
         CHECK(finite_all(sdq, 3 * 16) && finite_all(sdk, 3 * 16) && finite_all(sdv, 3 * 16));
     }

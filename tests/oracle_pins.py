@@ -444,6 +444,44 @@ def pin_bwd_sampled_matches_full(orc):
         _close(sv, dv[kc], tol=1e-12, what="sampled dV rows")
 
 
+def pin_bwd_d_from_given_o(orc):
+    # D formed from a given forward output O: with the exact O the gradients
+    # are torch's autograd ones (D = rowsum(P dP) = rowsum(dO O)); with O + E
+    # the closed form of the shift dD_i = sum_c dO_ic E_ic holds:
+    #   dQ_i changes by -scale dD_i (P K)_i,  dK_j by -scale sum_i P_ij dD_i q_i,  dV not at all
+    # (P from torch's float64 softmax); the row/column sampling entry agrees
+    import torch
+    rng = _rng(25)
+    for Nq, Nkv, d, causal, scale in [(11, 11, 6, True, 0.45), (7, 19, 5, True, -0.3), (9, 6, 8, False, 0.7)]:
+        q, do = rng.standard_normal((Nq, d)), rng.standard_normal((Nq, d))
+        k, v = rng.standard_normal((Nkv, d)), rng.standard_normal((Nkv, d))
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        s_ = scale * (tq @ tk.T)
+        if causal:
+            i = torch.arange(Nq)[:, None]
+            j = torch.arange(Nkv)[None, :]
+            s_ = s_.masked_fill(j > i + (Nkv - Nq), float("-inf"))
+        p = torch.softmax(s_, -1)
+        o = (p @ tv).numpy()
+        ref = _torch_attention_grads(q[None, None], k[None, None], v[None, None], do[None, None], causal, scale)
+        got = orc.attention_bwd(q, k, v, do, causal=causal, scale=scale, o_for_d=o)
+        for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+            _close(a, b[0, 0], tol=1e-11, what=f"{name} with D from the exact O")
+        e = rng.standard_normal((Nq, d)) * 1e-2
+        dd = np.sum(do * e, axis=1)
+        pn = p.numpy()
+        shifted = orc.attention_bwd(q, k, v, do, causal=causal, scale=scale, o_for_d=o + e)
+        _close(shifted[0] - got[0], -scale * dd[:, None] * (pn @ k), tol=1e-12, what="dQ shift from D")
+        _close(shifted[1] - got[1], -scale * (pn * dd[:, None]).T @ q, tol=1e-12, what="dK shift from D")
+        _close(shifted[2], got[2], tol=1e-13, what="dV independent of D")
+        qr = np.array([0, Nq - 1, Nq // 2], dtype=np.int64)
+        kc = np.array([Nkv - 1, 0, Nkv // 2], dtype=np.int64)
+        sq, sk, sv = orc.attention_bwd_sampled(q, k, v, do, qr, kc, causal=causal, scale=scale, o_for_d=o + e)
+        _close(sq, shifted[0][qr], tol=1e-12, what="sampled dQ rows, D from O")
+        _close(sk, shifted[1][kc], tol=1e-12, what="sampled dK rows, D from O")
+        _close(sv, shifted[2][kc], tol=1e-12, what="sampled dV rows, D from O")
+
+
 # ---------------------------------------------------------------------------
 # decode over a paged cache
 
@@ -635,7 +673,7 @@ PINS = [
     pin_constant_v, pin_q_zero, pin_causal_row0, pin_dominant_score, pin_single_key, pin_bounds,
     pin_linearity, pin_permutation, pin_shift_invariance, pin_merge_identity, pin_rows_match_full,
     pin_head_independence, pin_widened_inputs, pin_bwd_torch_autograd, pin_bwd_finite_difference,
-    pin_bwd_invariants, pin_bwd_sampled_matches_full, pin_paged_matches_dense, pin_paged_empty_and_single,
+    pin_bwd_invariants, pin_bwd_sampled_matches_full, pin_bwd_d_from_given_o, pin_paged_matches_dense, pin_paged_empty_and_single,
     pin_e4m3_decode_torch, pin_e4m3_quantize_torch, pin_e4m3_grid_and_saturation, pin_fp8_attention_identity,
     pin_fp8_attention_torch, pin_fp8_rows_match_full,
 ]

@@ -42,6 +42,13 @@ MUTANTS = [
      "acc_k += dS[i * Nkv + j] * dO[i * d + c];"),
     ("sampled backward drops D", "dsij = pij * (dp_ - Dv[i]);", "dsij = pij * dp_;"),
     ("sampled backward row term from the wrong row", "Dv[i] = Di;", "Dv[i] = Di * 0.5;"),
+    ("backward ignores the given O for D", "                Di += dO[i * d + c] * oD[i * d + c];\n        }\n        for (int64_t j = 0; j < Nkv; ++j)",
+     "                Di += 0.0 * oD[i * d + c];\n        }\n        for (int64_t j = 0; j < Nkv; ++j)"),
+    ("backward D from the given O of row 0", "                Di += dO[i * d + c] * oD[i * d + c];\n        }\n        for (int64_t j = 0; j < Nkv; ++j)",
+     "                Di += dO[i * d + c] * oD[c];\n        }\n        for (int64_t j = 0; j < Nkv; ++j)"),
+    ("sampled backward D from the given O with dO's sign flipped",
+     "                Di += dO[i * d + c] * oD[i * d + c];\n        }\n        Dv[i] = Di;",
+     "                Di -= dO[i * d + c] * oD[i * d + c];\n        }\n        Dv[i] = Di;"),
     ("paged layouts swapped", "const int64_t row = layout == 0 ?", "const int64_t row = layout == 1 ?"),
     ("paged head offset dropped", "? (page * H + h) * page_size + slot", "? (page * H) * page_size + slot"),
     ("paged slot shifted by one", "const int64_t slot = j % page_size;",
