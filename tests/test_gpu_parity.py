@@ -1,8 +1,9 @@
 """GPU parity: libfa355 against the fp64 oracle, through the C ABI.
 
-Small and ragged shapes are compared element by element; the full-size
-workloads (in the launch configuration the benchmark times) are compared on
-sampled rows that the oracle computes one at a time, plus properties that
+Small and ragged shapes are compared element by element, and so are the
+full-size workloads the benchmark times (in its launch configuration), with
+the oracle run one head at a time; larger and rectangular shapes are compared
+on sampled rows that the oracle computes one at a time, plus properties that
 hold at any size.  Every case prints its name before it touches the GPU.
 """
 import zlib
@@ -236,7 +237,9 @@ def _sample_rows(N, rng, extra=()):
 
 
 @pytest.mark.parametrize("name", ["prefill_8k_d128", "prefill_16k_d128_bf16"])
-def test_full_size_prefill_sampled(name):
+def test_full_size_prefill_every_element(name):
+    # every element of O and LSE of every head, against the oracle run one
+    # head at a time (one head's score matrix at a time in host memory)
     w = fi.WORKLOADS[name]
     say(f"generate {name}")
     x = fi.make_inputs(w)
@@ -246,24 +249,18 @@ def test_full_size_prefill_sampled(name):
     say(f"fa_fwd {name} fp32 O")
     o32, lse32 = fa.fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    # properties at every element: finite, native O is the rounded fp32 O
-    assert torch.isfinite(o32).all() and torch.isfinite(lse32).all()
+    # the native O is the rounded fp32 O, so its parity follows from the fp32 O's
     assert torch.equal(o16, o32.to(o16.dtype)) and torch.equal(lse16, lse32)
-    rng = np.random.default_rng(w.seed)
-    heads = sorted({0, w.heads // 2, w.heads - 1})
-    spikes = fi.spike_indices(w)
-    for bh in heads:
+    worst_o = worst_l = (0.0, None)
+    for bh in range(w.heads):
         b, h = divmod(bh, w.H)
-        extra = ()
-        if spikes:
-            j = spikes[bh]
-            extra = (j - 1, j, j + 1, j + 200)
-        rows = _sample_rows(w.Nq, rng, extra)
-        qh, kh, vh = x["q"][b, h], x["k"][b, h], x["v"][b, h]
-        o_ref, lse_ref = oracle.attention_rows(qh, kh, vh, rows, causal=w.causal, scale=w.scale, dtype=w.dtype)
-        o = to_np(o32[b, h][torch.from_numpy(rows).to(o32.device)])
-        lse = to_np(lse32[b, h][torch.from_numpy(rows).to(o32.device)])
-        check(o, lse, o_ref, lse_ref, w.dtype, f"{name} head {bh} rows {len(rows)}")
+        o_ref, lse_ref = oracle.attention(x["q"][b, h], x["k"][b, h], x["v"][b, h], causal=w.causal, scale=w.scale,
+                                          dtype=w.dtype)
+        eo, el = check(to_np(o32[b, h]), to_np(lse32[b, h]), o_ref, lse_ref, w.dtype,
+                       f"{name} head {bh}: all {w.Nq} rows")
+        worst_o, worst_l = max(worst_o, (eo, bh)), max(worst_l, (el, bh))
+    say(f"{name}: every element of {w.heads} heads within tolerance; worst err_O {worst_o[0]:.3e} (head "
+        f"{worst_o[1]}), worst err_LSE {worst_l[0]:.3e} (head {worst_l[1]})")
 
 
 WIDE_RECT = [
@@ -298,7 +295,8 @@ def test_wide_causal_rectangular_sampled(case):
         check(o8[b, h][rows], lse8[b, h][rows], o_ref, lse_ref, dtype, f"fwd_fp8 {case} head {bh}")
 
 
-def test_full_size_decode_sampled():
+def test_full_size_decode_every_head():
+    # all 512 heads, against the oracle run one head at a time
     w = fi.WORKLOADS["decode_32k_d128"]
     say("generate decode_32k_d128")
     x = fi.make_inputs(w)
@@ -308,16 +306,18 @@ def test_full_size_decode_sampled():
     say("fa_decode decode_32k_d128 fp32 O")
     o32, lse32 = fa.decode(tq, tk, tv, scale=w.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert torch.isfinite(o32).all() and torch.isfinite(lse32).all()
     assert torch.equal(o16, o32.to(o16.dtype)) and torch.equal(lse16, lse32)
-    rng = np.random.default_rng(w.seed)
-    heads = sorted(set(int(i) for i in rng.integers(0, w.heads, 24)) | {0, w.heads - 1})
     o_all, lse_all = to_np(o32), to_np(lse32)
-    for bh in heads:
+    o_ref = np.empty_like(o_all)
+    lse_ref = np.empty_like(lse_all)
+    for bh in range(w.heads):
         b, h = divmod(bh, w.H)
-        o_ref, lse_ref = oracle.attention_rows(x["q"][b, h], x["k"][b, h], x["v"][b, h], [0],
-                                               causal=False, scale=w.scale, dtype=w.dtype)
-        check(o_all[b, h], lse_all[b, h][None], o_ref, lse_ref, w.dtype, f"decode head {bh}")
+        if bh % 64 == 0:
+            say(f"oracle decode heads {bh}..{min(bh + 64, w.heads) - 1}")
+        ro, rl = oracle.attention(x["q"][b, h], x["k"][b, h], x["v"][b, h], causal=False, scale=w.scale,
+                                  dtype=w.dtype)
+        o_ref[b, h], lse_ref[b, h] = ro[0], rl[0]
+    check(o_all, lse_all, o_ref, lse_ref, w.dtype, f"decode, all {w.heads} heads")
 
 
 def test_spike_on_query_reading():
