@@ -115,10 +115,15 @@ void resolve_splits(int B, int H, int Nkv, int d, int requested, int *splits, in
     *splits = static_cast<int>((Nkv + c - 1) / c);
 }
 
-// Workgroups of a split decode: one per (b, h, split), at most INT_MAX.
+// Work-items of a split decode's launches: the split kernel runs 256 threads
+// per (b, h, split), the combine 512 per (b, h); each grid must stay within
+// HIP's 2^32 - 1 work-items.
+constexpr unsigned kDecodeSplitThreads = 256, kDecodeCombineThreads = 512;
 bool decode_grid_fits(int B, int H, int splits)
 {
-    return static_cast<unsigned __int128>(B) * H * splits <= 0x7fffffffU;
+    const unsigned __int128 bh = static_cast<unsigned __int128>(B) * H;
+    return bh * splits * kDecodeSplitThreads <= fa355::kMaxWorkItems &&
+           (splits == 1 || bh * kDecodeCombineThreads <= fa355::kMaxWorkItems);
 }
 
 }  // namespace
@@ -145,15 +150,13 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
     if (static_cast<unsigned long long>(Nkv) * d * 2 > 0xffffffffULL ||
         static_cast<unsigned long long>(Nq) * d * (out_f32 ? 4 : 2) > 0xffffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "%s: one head of q, k, v or o exceeds 4 GiB", fn);
-    const int rows = fa355::fwd_rows_per_block(d);
-    const long long blocks = static_cast<long long>(B) * H * ((Nq + rows - 1) / rows);
-    if (blocks > 0x7fffffffLL)
-        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
-
     fa355::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nkv, d, causal != 0, scale, elem, out_f32};
+    const unsigned long long items = fa355::fwd_work_items(a);
+    if (items > fa355::kMaxWorkItems)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %llu work-items exceed HIP's grid limit of 2^32 - 1", fn, items);
     if (log_enabled())
-        std::fprintf(stderr, "fa355: fa_fwd B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x grid=%lld\n",
-                     B, H, Nq, Nkv, d, causal != 0, dtype, blocks);
+        std::fprintf(stderr, "fa355: fa_fwd B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x work-items=%llu\n",
+                     B, H, Nq, Nkv, d, causal != 0, dtype, items);
     const hipError_t err = fa355::launch_fwd(a, stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
     return FA_OK;
@@ -179,16 +182,14 @@ int fa_fwd_fp8(const void *q, const void *k8, const void *v, void *o, float *lse
     if (static_cast<unsigned long long>(Nkv) * d * 2 > 0xffffffffULL ||
         static_cast<unsigned long long>(Nq) * d * (out_f32 ? 4 : 2) > 0xffffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "%s: one head of q, v or o exceeds 4 GiB", fn);
-    const int rows = fa355::fwd_rows_per_block(d);
-    const long long blocks = static_cast<long long>(B) * H * ((Nq + rows - 1) / rows);
-    if (blocks > 0x7fffffffLL)
-        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
-
     fa355::FwdArgs a{q, k8, v, o, lse, B, H, Nq, Nkv, d, causal != 0, scale, elem, out_f32};
     a.k_e4m3 = true;
+    const unsigned long long items = fa355::fwd_work_items(a);
+    if (items > fa355::kMaxWorkItems)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %llu work-items exceed HIP's grid limit of 2^32 - 1", fn, items);
     if (log_enabled())
-        std::fprintf(stderr, "fa355: fa_fwd_fp8 B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x grid=%lld\n", B,
-                     H, Nq, Nkv, d, causal != 0, dtype, blocks);
+        std::fprintf(stderr, "fa355: fa_fwd_fp8 B=%d H=%d Nq=%d Nkv=%d d=%d causal=%d dtype=0x%x work-items=%llu\n",
+                     B, H, Nq, Nkv, d, causal != 0, dtype, items);
     const hipError_t err = fa355::launch_fwd(a, stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
     return FA_OK;
@@ -230,11 +231,20 @@ int fa_decode_num_splits(int B, int H, int Nkv, int d)
     return splits;
 }
 
-int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nkv,
-              int d, float scale, int dtype, int num_splits, void *workspace, size_t workspace_bytes,
-              hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Validation of fa_decode, up to (not including)
+// the partials' storage.  Returns FA_OK with *work false when there is
+// nothing to do, else fills *a (without workspace) and *need (bytes of
+// partials the resolved split count uses; 0 with one split, which writes O
+// and LSE directly).
+int check_decode(const char *fn, const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                 int Nkv, int d, float scale, int dtype, int num_splits, fa355::DecodeArgs *a, size_t *need,
+                 bool *work)
 {
-    static const char *fn = "fa_decode";
+    *work = false;
     fa355::Elem elem;
     bool out_f32;
     int rc = parse_dtype(fn, dtype, &elem, &out_f32);
@@ -253,9 +263,38 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     int splits, chunk;
     resolve_splits(B, H, Nkv, d, num_splits, &splits, &chunk);
     if (!decode_grid_fits(B, H, splits))
-        return fail(FA_ERR_UNSUPPORTED, "%s: B*H*splits = %d*%d*%d workgroups exceed the grid limit", fn, B, H,
-                    splits);
-    const size_t need = fa355::decode_workspace_bytes(B, H, splits, d);
+        return fail(FA_ERR_UNSUPPORTED, "%s: B*H*splits = %d*%d*%d exceeds HIP's grid limit of 2^32 - 1 work-items",
+                    fn, B, H, splits);
+    *a = fa355::DecodeArgs{q, k, v, o, lse, B, H, Nkv, d, scale, elem, out_f32, splits, chunk, nullptr, nullptr};
+    *need = splits > 1 ? fa355::decode_workspace_bytes(B, H, splits, d) : 0;
+    *work = true;
+    return FA_OK;
+}
+
+// The partials of a split decode at ws: [B*H][splits][d] outputs, then
+// [B*H][splits] log-sum-exp values.
+void place_partials(fa355::DecodeArgs *a, void *ws)
+{
+    a->ws_o = static_cast<float *>(ws);
+    a->ws_lse = a->ws_o ? a->ws_o + static_cast<size_t>(a->B) * a->H * a->splits * a->d : nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nkv,
+              int d, float scale, int dtype, int num_splits, void *workspace, size_t workspace_bytes,
+              hipStream_t stream)
+{
+    static const char *fn = "fa_decode";
+    fa355::DecodeArgs a;
+    size_t partials;
+    bool work;
+    int rc = check_decode(fn, q, k, v, o, lse, B, H, Nkv, d, scale, dtype, num_splits, &a, &partials, &work);
+    if (rc || !work) return rc;
+    const bool out_f32 = a.out_f32;
+    const size_t need = fa355::decode_workspace_bytes(B, H, a.splits, d);
     if (!workspace || misaligned(workspace, 16) || workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)",
                     fn, need, workspace_bytes, workspace);
@@ -268,12 +307,10 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     for (const Span &s : others)
         if (s.hi > s.lo && overlap(ws, s)) return fail(FA_ERR_WORKSPACE, "%s: workspace overlaps %s", fn, s.name);
 
-    float *ws_o = static_cast<float *>(workspace);
-    float *ws_lse = ws_o + static_cast<size_t>(B) * H * splits * d;
-    fa355::DecodeArgs a{q, k, v, o, lse, B, H, Nkv, d, scale, elem, out_f32, splits, chunk, ws_o, ws_lse};
+    place_partials(&a, workspace);
     if (log_enabled())
         std::fprintf(stderr, "fa355: fa_decode B=%d H=%d Nkv=%d d=%d dtype=0x%x splits=%d chunk=%d\n", B, H,
-                     Nkv, d, dtype, splits, chunk);
+                     Nkv, d, dtype, a.splits, a.chunk);
     const hipError_t err = fa355::launch_decode(a, stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
     return FA_OK;
@@ -321,8 +358,8 @@ int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, con
     int splits, chunk;
     resolve_splits(B, H, max_seq_len, d, num_splits, &splits, &chunk);
     if (!decode_grid_fits(B, H, splits))
-        return fail(FA_ERR_UNSUPPORTED, "%s: B*H*splits = %d*%d*%d workgroups exceed the grid limit", fn, B, H,
-                    splits);
+        return fail(FA_ERR_UNSUPPORTED, "%s: B*H*splits = %d*%d*%d exceeds HIP's grid limit of 2^32 - 1 work-items",
+                    fn, B, H, splits);
     const size_t need = fa355::decode_workspace_bytes(B, H, splits, d);
     if (!workspace || misaligned(workspace, 16) || workspace_bytes < need)
         return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)",
@@ -412,9 +449,12 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const voi
     if (static_cast<unsigned long long>(Nkv) * d * oel > 0xffffffffULL ||
         static_cast<unsigned long long>(Nq) * d * oel > 0xffffffffULL)
         return fail(FA_ERR_UNSUPPORTED, "%s: one head of a tensor exceeds 4 GiB", fn);
-    const long long blocks = static_cast<long long>(B) * H * ((std::max(Nq, Nkv) + 127) / 128);
-    if (blocks > 0x7fffffffLL)
-        return fail(FA_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the grid limit", fn, blocks);
+    // the key-block and query-block passes: 256 threads per (b, h, 128-row
+    // block); the row-statistics pass is grid-stride with a capped grid
+    const unsigned long long items =
+        static_cast<unsigned long long>(B) * H * ((std::max(Nq, Nkv) + 127) / 128) * 256ULL;
+    if (items > fa355::kMaxWorkItems)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %llu work-items exceed HIP's grid limit of 2^32 - 1", fn, items);
     const size_t need = fa355::bwd_workspace_bytes(B, H, Nq);
     if (need && (!workspace || misaligned(workspace, 16) || workspace_bytes < need))
         return fail(FA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned and hold %zu bytes (got %zu at %p)", fn,

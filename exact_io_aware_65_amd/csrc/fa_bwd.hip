@@ -36,11 +36,13 @@
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace fa355 {
 namespace {
 
+constexpr long long kPrepMaxBlocks = 65536;  // prep grid cap (grid-stride beyond)
 constexpr float kBwdMinC = 1e-30f;  // as the forward: a zero scale keeps -inf * c = -inf
 
 struct BwdParams {
@@ -85,19 +87,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepParams p)
 {
     constexpr int LPR = D / 8, RPB = 256 / LPR;
     const int tid = threadIdx.x, part = tid % LPR;
-    const long long row = static_cast<long long>(blockIdx.x) * RPB + tid / LPR;
-    float acc = 0.f;
-    if (row < p.rows) {
-        const size_t off = static_cast<size_t>(row) * D * 2 + part * 16;
-        const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.o) + off);
-        const u32x4 g = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.dout) + off);
+    // grid-stride over blocks of RPB rows (the grid is capped on the host);
+    // the bound is the same for every lane of a row group, so the DPP sum
+    // below always runs with whole groups
+    const long long stride = static_cast<long long>(gridDim.x) * RPB;
+    for (long long row = static_cast<long long>(blockIdx.x) * RPB + tid / LPR; row - tid / LPR < p.rows;
+         row += stride) {
+        float acc = 0.f;
+        if (row < p.rows) {
+            const size_t off = static_cast<size_t>(row) * D * 2 + part * 16;
+            const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.o) + off);
+            const u32x4 g = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.dout) + off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = dot2<T>(o[j], g[j], acc);
-    }
-    acc = group_sum<LPR>(acc);
-    if (part == 0 && row < p.rows) {
-        p.dd[row] = acc;
-        p.l2[row] = p.lse[row] * kLog2e;
+            for (int j = 0; j < 4; ++j) acc = dot2<T>(o[j], g[j], acc);
+        }
+        acc = group_sum<LPR>(acc);
+        if (part == 0 && row < p.rows) {
+            p.dd[row] = acc;
+            p.l2[row] = p.lse[row] * kLog2e;
+        }
     }
 }
 
@@ -510,8 +518,8 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
     if (rows > 0) {
         PrepParams pp{a.o, a.dout, a.lse, a.ws_l2, a.ws_dd, rows};
         constexpr int RPB = 256 / (D / 8);
-        hipLaunchKernelGGL((bwd_prep_kernel<D, T>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)), dim3(256), 0,
-                           stream, pp);
+        const long long blocks = std::min<long long>((rows + RPB - 1) / RPB, kPrepMaxBlocks);
+        hipLaunchKernelGGL((bwd_prep_kernel<D, T>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, pp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
 

@@ -641,18 +641,20 @@ hipError_t launch_shape(const FwdArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int D, typename T, bool CAUSAL, bool OUT_F32, bool KF8>
-hipError_t launch_k(const FwdArgs &a, hipStream_t stream)
+// The launch shape of a call: waves per workgroup and key groups.
+struct Shape {
+    int nw, kg;
+};
+
+Shape pick_shape(const FwdArgs &a)
 {
     // E4M3 K: the 4-wave shape only.  Its first product is a quarter of the
     // 16-bit one, so phase 1 is VALU-bound, and two workgroups per CU (whose
     // waves do not share barriers) overlap one wave's softmax with the other's
     // MFMAs better than one 8-wave workgroup: measured 4% faster at 8K d=128.
     // (A d = 64 E4M3 K tile is also exactly one load per thread of 4 waves.)
-    constexpr bool kWide = !KF8;
     const long long wide_blocks = static_cast<long long>(a.B) * a.H * ((a.Nq + 255) / 256);
-    if constexpr (kWide)
-        if (wide_blocks >= kCUs) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8>(a, stream);
+    if (!a.k_e4m3 && wide_blocks >= kCUs) return {8, 1};
     // Too few 128-row tiles to give every CU one: two key groups per tile
     // halve the serial chain of key tiles (worth it from 4 key tiles on).
     // Causal at d = 64 (16-bit K): 64-row tiles of two 2-wave key groups.
@@ -662,9 +664,21 @@ hipError_t launch_k(const FwdArgs &a, hipStream_t stream)
     // mask the tiles are even, and the 128-row shape is 4-5% faster.
     const long long tiles = static_cast<long long>(a.B) * a.H * ((a.Nq + 127) / 128);
     if (tiles <= kCUs && a.Nkv > 3 * kBN) {
-        if constexpr (CAUSAL && D == 64 && !KF8) return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2, KF8, 2>(a, stream);
-        return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8, 2>(a, stream);
+        if (a.causal && a.d == 64 && !a.k_e4m3) return {4, 2};
+        return {8, 2};
     }
+    return {4, 1};
+}
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32, bool KF8>
+hipError_t launch_k(const FwdArgs &a, hipStream_t stream)
+{
+    const Shape s = pick_shape(a);
+    if constexpr (!KF8)
+        if (s.nw == 8 && s.kg == 1) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8>(a, stream);
+    if constexpr (CAUSAL && D == 64 && !KF8)
+        if (s.nw == 4 && s.kg == 2) return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2, KF8, 2>(a, stream);
+    if (s.nw == 8 && s.kg == 2) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8, 2>(a, stream);
     return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2, KF8>(a, stream);
 }
 
@@ -691,9 +705,12 @@ hipError_t launch_d(const FwdArgs &a, hipStream_t stream)
 
 }  // namespace
 
-// The smallest workgroup (rows) any launch shape uses: the grid bound check
-// in the ABI layer is conservative with it.
-int fwd_rows_per_block(int) { return 64; }
+unsigned long long fwd_work_items(const FwdArgs &a)
+{
+    const Shape s = pick_shape(a);
+    const long long rows = 32LL * s.nw / s.kg;
+    return static_cast<unsigned long long>(a.B) * a.H * ((a.Nq + rows - 1) / rows) * (64ULL * s.nw);
+}
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream)
 {

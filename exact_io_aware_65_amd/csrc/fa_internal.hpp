@@ -57,8 +57,10 @@ struct BwdArgs {
     float *ws_dd;  // [B*H][Nq] rowsum(dO * O)
 };
 
-// Query rows handled by one prefill workgroup (depends on d).
-int fwd_rows_per_block(int d);
+// Work-items (workgroups x threads) of the forward's launch for these
+// arguments: HIP takes at most 2^32 - 1 in one grid dimension.
+unsigned long long fwd_work_items(const FwdArgs &a);
+constexpr unsigned long long kMaxWorkItems = 0xffffffffULL;
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

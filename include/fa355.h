@@ -163,7 +163,8 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace fa_decode needs for these arguments (0 if they are invalid,
- * or if B * H * splits exceeds INT_MAX, which fa_decode rejects). */
+ * or if the split kernel's grid, B * H * splits workgroups of 256 threads,
+ * would exceed HIP's 2^32 - 1 work-items, which fa_decode rejects). */
 size_t fa_decode_workspace_size(int B, int H, int Nkv, int d, int num_splits);
 
 /* The split count fa_decode uses for num_splits = 0 (0 if the arguments are invalid). */

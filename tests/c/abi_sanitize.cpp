@@ -84,6 +84,10 @@ int main()
     expect(fa_decode(q, k, v, o, lse, INT_MAX, INT_MAX, INT_MAX, 128, 0.1f, FA_F16, 0, ws, need, nullptr),
            FA_ERR_INVALID, "decode 2^62");
 
+    // 2^24 heads of one key (one split each): 2^32 work-items, one beyond HIP's grid limit
+    expect(fa_decode(q, k, v, o, lse, 1 << 12, 1 << 12, 1, 64, 0.1f, FA_F16, 1, ws, SIZE_MAX, nullptr),
+           FA_ERR_UNSUPPORTED, "decode grid 2^32");
+
     // paged decode
     const std::size_t pneed = fa_decode_workspace_size(3, 5, 300, 64, 0);
     expect(fa_decode_paged(q, k, v, table, lens, o, lse, 3, 5, 64, 97, 16, 19, FA_PAGED_HND, 300, 0.1f, FA_F16, 0,
@@ -121,13 +125,28 @@ int main()
                   bneed, nullptr),
            FA_ERR_INVALID, "bwd 2^62");
 
+    // 2^23 + 2^12 one-row heads: as many 8-wave workgroups of 512 threads
+    // (forward), 2^32 + 2^21 work-items; 2^24 one-row heads in the backward's
+    // 256-thread passes, 2^32: both beyond HIP's 2^32 - 1
+    expect(fa_fwd(q, k, v, o, lse, 1 << 12, (1 << 11) + 1, 1, 1, 64, 0, 0.1f, FA_F16, nullptr), FA_ERR_UNSUPPORTED,
+           "fwd grid 2^32 + 2^21");
+    expect(fa_fwd(q, k, v, o, lse, 1 << 12, (1 << 11) - 1, 1, 1, 64, 0, 0.1f, FA_F16, nullptr), FA_OK,
+           "fwd grid 2^32 - 2^21");
+    expect(fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, 1 << 12, 1 << 12, 1, 1, 64, 0, 0.1f, FA_F16, ws, SIZE_MAX,
+                  nullptr),
+           FA_ERR_UNSUPPORTED, "bwd grid 2^32");
+
     // size helpers at the extremes: no signed overflow, no wrapped sizes
     if (fa_decode_num_splits(INT_MAX, INT_MAX, INT_MAX, 64) < 1) ++failures;
     if (fa_decode_num_splits(1, 1, INT_MAX, 128) < 1) ++failures;
-    // INT_MAX one-key splits of one head: exactly the grid limit
-    if (fa_decode_workspace_size(1, 1, INT_MAX, 64, INT_MAX) != static_cast<std::size_t>(INT_MAX) * 65 * 4)
+    // 2^24 - 1 one-key splits of one head, 256 threads each: just within HIP's
+    // 2^32 - 1 work-items; one more split, or INT_MAX of them, is beyond it
+    if (fa_decode_workspace_size(1, 1, ((1 << 24) - 1) * 128, 64, (1 << 24) - 1) !=
+        static_cast<std::size_t>((1 << 24) - 1) * 65 * 4)
         ++failures;
-    if (fa_decode_workspace_size(2, 1, INT_MAX, 64, INT_MAX) != 0) ++failures;  // twice the limit
+    if (fa_decode_workspace_size(1, 1, INT_MAX, 64, 1 << 24) != 0) ++failures;
+    if (fa_decode_workspace_size(1, 1, INT_MAX, 64, INT_MAX) != 0) ++failures;
+    if (fa_decode_workspace_size(2, 1, INT_MAX, 64, INT_MAX) != 0) ++failures;
     if (fa_decode_workspace_size(INT_MAX, INT_MAX, INT_MAX, 128, INT_MAX) != 0) ++failures;
     if (fa_decode_workspace_size(4, 8, 1000, 64, INT_MAX) != static_cast<std::size_t>(4) * 8 * 1000 * 65 * 4)
         ++failures;

@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_num_splits", "fa_decode_paged",
-        "fa_decode_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_last_error", "fa_status_str", "fa_version"])
+        "fa_decode_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_last_error",
+        "fa_status_str", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
