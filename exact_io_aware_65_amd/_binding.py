@@ -6,7 +6,7 @@ stream.  The library must have been built (``python -m
 exact_io_aware_65_amd.build``); there is no fallback of any kind.
 
 Thin wrappers with the C names (``fa_fwd``, ``fa_fwd_fp8``, ``fa_decode``,
-``fa_decode_paged``, ``fa_bwd``, ...)
+``fa_decode_noalloc``, ``fa_decode_paged``, ``fa_bwd``, ...)
 take device pointers or tensors and raise :class:`FaError` on a non-OK
 status.  The convenience functions :func:`fwd`, :func:`fwd_fp8`,
 :func:`quantize_e4m3`, :func:`decode`, :func:`decode_paged` and :func:`bwd`
@@ -28,6 +28,7 @@ FA_OUT_F32 = 0x100
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 FA_PAGED_HND = 0  # pages [num_pages, H, page_size, d]
 FA_PAGED_NHD = 1  # pages [num_pages, page_size, H, d]
+FA_DECODE_NOALLOC_SCRATCH_BYTES = 4 << 20  # fa_decode_noalloc's device scratch
 
 
 class FaError(RuntimeError):
@@ -51,6 +52,8 @@ def library() -> ctypes.CDLL:
         lib.fa_fwd.restype = i
         lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
         lib.fa_decode.restype = i
+        lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+        lib.fa_decode_noalloc.restype = i
         lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i]
         lib.fa_decode_workspace_size.restype = ctypes.c_size_t
         lib.fa_decode_num_splits.argtypes = [i, i, i, i]
@@ -113,6 +116,11 @@ def fa_decode(q, k, v, o, lse, B, H, Nkv, d, scale, dtype, num_splits, workspace
     _check(library().fa_decode(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, H, Nkv, d,
                                float(scale), int(dtype), int(num_splits), _addr(workspace),
                                int(workspace_bytes), _addr(stream)))
+
+
+def fa_decode_noalloc(q, k, v, o, lse, B, H, Nkv, d, scale, dtype, num_splits, stream=None) -> None:
+    _check(library().fa_decode_noalloc(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), B, H, Nkv, d,
+                                       float(scale), int(dtype), int(num_splits), _addr(stream)))
 
 
 def fa_decode_workspace_size(B, H, Nkv, d, num_splits=0) -> int:

@@ -14,6 +14,8 @@
 
 #include "fa_internal.hpp"
 
+static_assert(FA_DECODE_NOALLOC_SCRATCH_BYTES == fa355::kDecodeScratchBytes, "the header states the scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -235,7 +237,7 @@ int fa_decode_num_splits(int B, int H, int Nkv, int d)
 
 namespace {
 
-// Validation of fa_decode, up to (not including)
+// Validation shared by fa_decode and fa_decode_noalloc, up to (not including)
 // the partials' storage.  Returns FA_OK with *work false when there is
 // nothing to do, else fills *a (without workspace) and *need (bytes of
 // partials the resolved split count uses; 0 with one split, which writes O
@@ -310,6 +312,35 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse, 
     place_partials(&a, workspace);
     if (log_enabled())
         std::fprintf(stderr, "fa355: fa_decode B=%d H=%d Nkv=%d d=%d dtype=0x%x splits=%d chunk=%d\n", B, H,
+                     Nkv, d, dtype, a.splits, a.chunk);
+    const hipError_t err = fa355::launch_decode(a, stream);
+    if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));
+    return FA_OK;
+}
+
+int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Nkv,
+                      int d, float scale, int dtype, int num_splits, hipStream_t stream)
+{
+    static const char *fn = "fa_decode_noalloc";
+    fa355::DecodeArgs a;
+    size_t need;
+    bool work;
+    int rc = check_decode(fn, q, k, v, o, lse, B, H, Nkv, d, scale, dtype, num_splits, &a, &need, &work);
+    if (rc || !work) return rc;
+    if (need > fa355::kDecodeScratchBytes)
+        return fail(FA_ERR_WORKSPACE,
+                    "%s: %d*%d heads x %d splits need %zu bytes of partials, beyond the %zu-byte device scratch "
+                    "(call fa_decode with a workspace, or pass fewer splits)",
+                    fn, B, H, a.splits, need, fa355::kDecodeScratchBytes);
+    void *scratch = nullptr;
+    if (need > 0) {
+        const hipError_t err = fa355::decode_scratch(&scratch);
+        if (err != hipSuccess)
+            return fail(FA_ERR_HIP, "%s: device scratch lookup failed: %s", fn, hipGetErrorString(err));
+    }
+    place_partials(&a, scratch);
+    if (log_enabled())
+        std::fprintf(stderr, "fa355: fa_decode_noalloc B=%d H=%d Nkv=%d d=%d dtype=0x%x splits=%d chunk=%d\n", B, H,
                      Nkv, d, dtype, a.splits, a.chunk);
     const hipError_t err = fa355::launch_decode(a, stream);
     if (err != hipSuccess) return fail(FA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(err));

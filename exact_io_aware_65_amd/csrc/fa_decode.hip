@@ -35,6 +35,7 @@
 #include "fa_internal.hpp"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace fa355 {
@@ -388,6 +389,35 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 }
 
 }  // namespace
+
+// Scratch of fa_decode_noalloc: the split partials of one call live in this
+// file-scope device array instead of a caller workspace, so that callers that
+// cannot allocate device memory can still run a split decode.  Each device
+// holds its own copy for the life of the process.  In host code the array's
+// name is only a stand-in: its device address comes from hipGetSymbolAddress,
+// looked up once per device and kept below.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int decode_auto_splits(int B, int H, int Nkv, int /*d*/)
 {

@@ -77,6 +77,12 @@ inline std::size_t bwd_workspace_bytes(int B, int H, int Nq)
 // Split count used when the caller passes num_splits = 0.
 int decode_auto_splits(int B, int H, int Nkv, int d);
 
+// Size of the device-resident scratch fa_decode_noalloc uses in place of a
+// workspace (4 MiB per device), and its device address on the current device
+// (looked up once per device; no allocation).
+constexpr std::size_t kDecodeScratchBytes = std::size_t(4) << 20;
+hipError_t decode_scratch(void **ptr);
+
 // Workspace bytes for a resolved split count.
 inline std::size_t decode_workspace_bytes(int B, int H, int splits, int d)
 {

@@ -41,8 +41,9 @@
  * Ownership.  Every pointer is device memory owned by the caller (for example
  * the storage of framework tensors).  The library allocates no device memory:
  * fa_fwd, fa_fwd_fp8 and fa_quantize_e4m3 need none; fa_decode,
- * fa_decode_paged and fa_bwd use only the caller's workspace.  No pointer is
- * retained after a call returns.
+ * fa_decode_paged and fa_bwd use only the caller's workspace; fa_decode_noalloc
+ * uses a fixed device-resident scratch array of the library instead.  No
+ * pointer is retained after a call returns.
  *
  * Execution.  Calls enqueue work on `stream` (NULL = the default stream) and
  * return without waiting; results are ready when the stream is synchronised.
@@ -83,7 +84,7 @@ extern "C" {
 /* HIP's opaque stream handle (identical to the typedef in hip_runtime_api.h). */
 typedef struct ihipStream_t *hipStream_t;
 
-#define FA355_VERSION 4
+#define FA355_VERSION 5
 
 /* Element type of q, k, v (and of o unless FA_OUT_F32 is set). */
 enum fa_dtype {
@@ -161,6 +162,33 @@ int fa_quantize_e4m3(const void *x, void *y, size_t n, int dtype, hipStream_t st
 int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
               int B, int H, int Nkv, int d, float scale, int dtype, int num_splits,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_decode for callers that cannot allocate device memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * same computation, kernels and split rule as fa_decode (bit-identical
+ * results for the same arguments), with the split partials kept in a
+ * device-resident scratch array of the library instead of a caller
+ * workspace.  The caller still passes q, k, v, o and lse as for fa_decode.
+ *
+ * The scratch is 4 MiB (FA_DECODE_NOALLOC_SCRATCH_BYTES) per device, held
+ * from the library's first use on that device until the process ends; a call
+ * whose partials, B * H * splits * (d + 1) * 4 bytes (none with one split),
+ * would not fit returns FA_ERR_WORKSPACE before touching the device (at the
+ * automatic split count every call with B * H <= 2048 fits).  The scratch's
+ * address is looked up once per device, on that device's first call (which
+ * therefore should not itself be under graph capture).  The call allocates
+ * nothing and frees nothing.
+ *
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap in time on one device (different streams, different host threads
+ * without ordering) race on it and give undefined results; calls ordered on
+ * one stream are safe.  The contents left by an earlier call are never read.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int B, int H, int Nkv, int d, float scale, int dtype, int num_splits,
+                      hipStream_t stream);
 
 /* Bytes of workspace fa_decode needs for these arguments (0 if they are invalid,
  * or if the split kernel's grid, B * H * splits workgroups of 256 threads,

@@ -84,6 +84,16 @@ int main()
     expect(fa_decode(q, k, v, o, lse, INT_MAX, INT_MAX, INT_MAX, 128, 0.1f, FA_F16, 0, ws, need, nullptr),
            FA_ERR_INVALID, "decode 2^62");
 
+    // decode without a workspace: partials in the library's device scratch
+    expect(fa_decode_noalloc(q, k, v, o, lse, 3, 5, 7777, 128, 0.1f, FA_F16, 0, nullptr), FA_OK, "decode noalloc");
+    expect(fa_decode_noalloc(q, k, v, o, lse, 64, 64, 100, 128, 0.1f, FA_F16, 1, nullptr), FA_OK,
+           "decode noalloc one split (no scratch)");
+    expect(fa_decode_noalloc(q, k, v, o, lse, 16, 32, 32768, 128, 0.1f, FA_F16, 64, nullptr), FA_ERR_WORKSPACE,
+           "decode noalloc beyond the scratch");
+    expect(fa_decode_noalloc(q, k, v, q, lse, 3, 5, 7777, 128, 0.1f, FA_F16, 0, nullptr), FA_ERR_INVALID,
+           "decode noalloc overlap");
+    expect(fa_decode_noalloc(nullptr, nullptr, nullptr, nullptr, nullptr, 0, 5, 7777, 128, 0.1f, FA_F16, 0, nullptr),
+           FA_OK, "decode noalloc empty");
     // 2^24 heads of one key (one split each): 2^32 work-items, one beyond HIP's grid limit
     expect(fa_decode(q, k, v, o, lse, 1 << 12, 1 << 12, 1, 64, 0.1f, FA_F16, 1, ws, SIZE_MAX, nullptr),
            FA_ERR_UNSUPPORTED, "decode grid 2^32");

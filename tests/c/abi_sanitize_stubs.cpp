@@ -30,6 +30,13 @@ unsigned long long fwd_work_items(const FwdArgs &a)
     return static_cast<unsigned long long>(bh) * ((a.Nq + rows - 1) / rows) * (64ULL * nw);
 }
 
+// A fake, aligned device address for the no-allocation decode's scratch.
+hipError_t decode_scratch(void **ptr)
+{
+    *ptr = reinterpret_cast<void *>(std::uintptr_t(13) << 36);
+    return hipSuccess;
+}
+
 // The library's rule for the automatic split count, restated so that this
 // host-only program links no device code.
 int decode_auto_splits(int B, int H, int Nkv, int)

@@ -36,7 +36,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_num_splits", "fa_decode_paged",
-        "fa_decode_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_last_error",
+        "fa_decode_noalloc", "fa_decode_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_quantize_e4m3", "fa_last_error",
         "fa_status_str", "fa_version"])
 
 
@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert fa.fa_version() == 4
+    assert fa.fa_version() == 5
     assert [fa.fa_status_str(s) for s in range(5)] == [
         "FA_OK", "FA_ERR_INVALID", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP"]
     assert fa.fa_status_str(99) == "FA_ERR_UNKNOWN"
@@ -162,6 +162,34 @@ def test_decode_rejects(kw, status, needle):
     got, msg = dec(**kw)
     assert got == status, (got, msg)
     assert needle in msg, msg
+
+
+def dec_noalloc(q=A, k=B_, v=C, o=O, lse=L, B=2, H=2, Nkv=1000, d=128, scale=0.1, dtype=fa.FA_F16, splits=0):
+    return status_of(fa.fa_decode_noalloc, q, k, v, o, lse, B, H, Nkv, d, scale, dtype, splits, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED, "d=80"),
+    (dict(Nkv=0), fa.FA_ERR_INVALID, "no keys"),
+    (dict(splits=-1), fa.FA_ERR_INVALID, "num_splits"),
+    (dict(o=B_), fa.FA_ERR_INVALID, "o overlaps k"),
+    (dict(dtype=0), fa.FA_ERR_INVALID, "dtype"),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID, "finite"),
+    # 512 heads x 64 splits x (128 + 1) floats = 16.9 MB of partials > the 4 MiB scratch
+    (dict(B=16, H=32, Nkv=32768, splits=64), fa.FA_ERR_WORKSPACE, "device scratch"),
+])
+def test_decode_noalloc_rejects(kw, status, needle):
+    got, msg = dec_noalloc(**kw)
+    assert got == status, (got, msg)
+    assert needle in msg, msg
+
+
+def test_decode_noalloc_scratch_bound():
+    # every automatic split count up to 2048 heads fits the scratch at d = 128
+    for bh in (1, 7, 64, 512, 513, 700, 1024, 2048):
+        need = fa.fa_decode_workspace_size(1, bh, 1 << 20, 128, 0)
+        assert 0 < need <= fa.FA_DECODE_NOALLOC_SCRATCH_BYTES, (bh, need)
+    assert dec_noalloc(B=0, q=None, k=None, v=None, o=None, lse=None)[0] == fa.FA_OK
 
 
 TB = 11 << 32
