@@ -44,6 +44,18 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(16x16, fp32) += A(16x32) * B(32x16).  Lane l supplies row (A) or column
+// (B) l % 16 and eight k-slots chosen by l / 16, the same way for A and B; it
+// receives column l % 16 of D, rows 4 (l / 16) .. + 3.
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // FP8 operands: 32 E4M3 bytes per lane.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -80,6 +92,22 @@ template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b)
 {
     bf16x2 v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + the low / high binary16 element of w, widened exactly (one
+// v_fma_mix_f32 with a 1.0 multiplier; a plain VALU instruction, unlike the
+// packed dot products, which share the matrix pipeline).
+__device__ __forceinline__ float add_lo_f16(float acc, uint32_t w)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(acc));
+    return r;
+}
+__device__ __forceinline__ float add_hi_f16(float acc, uint32_t w)
+{
+    float r;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(acc));
+    return r;
 }
 
 // Widen the low / high 16-bit element of a packed word to fp32 (exact).
@@ -141,12 +169,18 @@ __device__ __forceinline__ u32x4 make_rsrc_words(const void *base, uint32_t byte
 // wait_vmcnt<N>() before a barrier that publishes the data.  The LDS offset
 // of a shared-memory pointer is the low 32 bits of its flat address (the
 // aperture is 4 GiB aligned).
+//
+// The compiler does not look inside the asm for hazards, so the asm pads for
+// them itself: an SGPR operand (the descriptor, the offset or M0) may have
+// just been written by a VALU instruction -- for instance reloaded with
+// v_readlane from a spill lane -- and a VMEM read of an SGPR written by VALU
+// needs 5 wait states (s_nop 4).
 template <int IMM = 0>
 __device__ __forceinline__ void dma_to_lds16(u32x4 rsrc, uint32_t voff, uint32_t soff, const void *lds_base)
 {
     static_assert(IMM >= 0 && IMM < 4096, "12-bit instruction offset");
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%4 lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(m0), "n"(IMM)
                  : "memory");
@@ -159,7 +193,7 @@ __device__ __forceinline__ void dma_to_lds4(u32x4 rsrc, uint32_t voff, uint32_t 
 {
     static_assert(IMM >= 0 && IMM < 4096, "12-bit instruction offset");
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen offset:%4 lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen offset:%4 lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(m0), "n"(IMM)
                  : "memory");

@@ -608,6 +608,568 @@ void fwd_kernel(FwdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same algorithm on the 16x16x32 MFMA, for 16-bit K.
+//
+// Measured on MI355X with random fp16 operands at two waves per SIMD, a stream
+// of v_mfma_f32_16x16x32_f16 sustains about 18% more FLOP/s than one of
+// v_mfma_f32_32x32x16_f16 (1876 against 1592 TFLOP/s), while on all-zero
+// operands the two are equal (2352 / 2322): the smaller instruction moves a
+// quarter of the accumulator per issue, and under the chip's power limit the
+// energy per FLOP sets the rate.  This kernel keeps the 32x32 kernel's
+// structure -- 32 query rows per wave, 64-key tiles through a direct-to-LDS
+// ring, heavy tiles first -- and changes the fragment layout and the
+// schedule (below):
+//
+//   S^T (16 keys x 16 queries) += K (16 keys x 32 dims) * Q^T (32 dims x 16 queries)
+//   O^T (16 dims x 16 queries) += V^T (16 dims x 32 keys) * P^T (32 keys x 16 queries)
+//
+// Lane l = 16 g + i supplies row / column i of an operand and the eight
+// k-slots of group g; it receives column i (a query) and rows 4g .. 4g + 3 of
+// the result.  A wave's 32 rows are two query blocks, so a lane holds two
+// queries and, per 64-key tile, the keys {16 kb + 4 g + r : kb < 4, r < 4} of
+// each.  Each K or V^T operand read from LDS feeds both query blocks (the same
+// LDS bytes per FLOP as the 32x32 kernel).  A k-step of the second product
+// takes key blocks 2s and 2s + 1, and a lane's k-slots are keys 4g .. 4g + 3 of
+// each -- the keys its score fragments already hold -- so P goes from the
+// score accumulators to the MFMA operand without moving between lanes.
+//
+// Row maxima are taken on demand.  Probabilities are formed against the
+// reference maximum in use (m_run, the same for the four lanes of a query);
+// the tile is redone against the running maximum only when some lane's sum
+// over its keys exceeds kSumLimit or is not finite (a wave-uniform branch:
+// the first tile of every row, and a row whose scores later rise by more than
+// about 2^15 over the reference).  So every probability of a 16-bit P operand
+// is at most kSumLimit, far inside its range, and the common step has no
+// cross-lane reduction at all: the four lanes' partial row sums meet only in
+// the epilogue.  O = acc / l is exact whatever the reference, as numerator and
+// denominator share it.
+//
+// Schedule of the eight-wave shape (two waves per SIMD).  A wave's work per
+// key tile splits into an MFMA block M (the next tile's scores and this
+// tile's O += V P: 64 MFMAs at d = 128, no VALU beyond addressing) and a VALU
+// block (softmax of the scores just formed: about 110 instructions, a third
+// of them v_exp_f32).  A single wave issues at most one VALU instruction per
+// ~8 cycles, while an MFMA stream of another wave on the same SIMD keeps
+// running beside it at nearly full rate (measured: 17 cycles per 16x16x32
+// MFMA beside a stream of FMAs, 19 beside exps, 16 alone).  So the two waves
+// of a SIMD are kept half a step apart: waves 0..3 pass the step's barrier
+// after their softmax block and waves 4..7 after their MFMA block, and each
+// SIMD's MFMA block of one wave runs beside the softmax block of the other.
+// Measured 4-6% faster than running both waves through the same phases on
+// the causal 8K and 16K d = 128 workloads; the M block requests its LDS
+// operands a fixed distance ahead of the MFMAs that take them (K one k-step,
+// V six MFMA pairs ahead): another 2-7%.
+constexpr float kSumLimit = 32768.0f;
+
+// V rows are read transposed: a 32-lane group covers 8 consecutive rows x 32
+// bytes; the permutation puts those 8 runs into 8 distinct 32-byte segments of
+// the 256-byte bank line (two rows share a line at d = 64).
+template <int D> __host__ __device__ constexpr int vswz16(int row)
+{
+    return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
+}
+template <int ROWB, int LOADS, int NW, int (*SWZ)(int)> constexpr bool load_xor_holds(int (*xor_of)(int))
+{
+    constexpr int DCH = ROWB / 16;
+    for (int w = 0; w < NW; ++w)
+        for (int lane = 0; lane < 64; ++lane) {
+            const int row = (w * LOADS * 64 + lane) / DCH;
+            for (int i = 0; i < LOADS; ++i)
+                if (SWZ(row + i * (1024 / ROWB)) != (SWZ(row) ^ xor_of(i))) return false;
+        }
+    return true;
+}
+template <int ROWB> constexpr int k16_xor(int i) { return kswz<ROWB>(i * (1024 / ROWB)); }
+template <int D> constexpr int v16_xor(int i) { return vswz16<D>(i * (1024 / (2 * D))); }
+template <int ROWB> constexpr int kswz_fn(int row) { return kswz<ROWB>(row); }
+template <int D> constexpr int vswz16_fn(int row) { return vswz16<D>(row); }
+
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd16_kernel(FwdParams p)
+{
+    constexpr int BN = kBN, BM = 32 * NW;  // keys per tile, query rows per workgroup
+    constexpr int NT = 64 * NW;            // threads (they fill the ring)
+    constexpr int DC = D / 8;              // 16-byte chunks per row
+    constexpr int TILE = BN * DC;          // chunks per K or V tile
+    constexpr int LOADS = TILE / NT;       // direct loads per thread per tile
+    constexpr int ROWB = D * 2;            // bytes per row
+    constexpr int KS = D / 32;             // k-steps of the first product
+    constexpr int DB = D / 16;             // 16-dim blocks of the output
+    constexpr int U = lcm2(NS);
+    static_assert(NS >= 2 && TILE % NT == 0 && LOADS >= 1 && LOADS <= 4, "tile must split evenly over the threads");
+    static_assert(load_xor_holds<ROWB, LOADS, NW, kswz_fn<ROWB>>(k16_xor<ROWB>), "K load i is load 0 re-permuted");
+    static_assert(load_xor_holds<ROWB, LOADS, NW, vswz16_fn<D>>(v16_xor<D>), "V load i is load 0 re-permuted");
+    static_assert(NS * TILE * 16 <= 65536, "stage offsets must fit the 16-bit LDS immediate");
+    using V8 = typename Vec<T>::v8;
+
+    __shared__ u32x4 lds_rings[NS * 2 * TILE];
+    u32x4(*const sk)[TILE] = reinterpret_cast<u32x4(*)[TILE]>(lds_rings);
+    u32x4(*const sv)[TILE] = reinterpret_cast<u32x4(*)[TILE]>(lds_rings + NS * TILE);
+    if constexpr (kPoisonLds) {
+        poison_lds(lds_rings, sizeof(lds_rings));
+        __syncthreads();
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, li = lane & 15;
+
+    const int bh = blockIdx.x % p.n_bh;
+    const int qt = p.n_qt - 1 - static_cast<int>(blockIdx.x / p.n_bh);
+    const int q0 = qt * BM;
+    const int wq0 = q0 + 32 * wave;
+    const int off = p.Nkv - p.Nq;
+    int kend = p.Nkv;
+    if constexpr (CAUSAL) kend = min(p.Nkv, min(q0 + BM, p.Nq) + off);
+    const int nkb = (kend + BN - 1) / BN;
+    int nkw = 0;
+    if (wq0 < p.Nq) {
+        nkw = nkb;
+        if constexpr (CAUSAL) nkw = min(nkb, (min(wq0 + 31, p.Nq - 1) + off) / BN + 1);
+    }
+
+    const size_t q_head = static_cast<size_t>(bh) * p.Nq * ROWB;
+    const size_t kv_head = static_cast<size_t>(bh) * p.Nkv * ROWB;
+    const auto rq = make_rsrc(static_cast<const char *>(p.q) + q_head, static_cast<uint32_t>(p.Nq) * ROWB);
+    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
+    const u32x4 rv = make_rsrc_words(static_cast<const char *>(p.v) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
+
+    // Q operand, loaded once: lane (g, i) holds query wq0 + 16 qb + i, dims
+    // 32 s + 8 g .. + 7.
+    V8 qf[2][KS];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const u32x4 x = buffer_load16(rq, static_cast<uint32_t>(wq0 + 16 * qb + li) * ROWB + (32 * s + 8 * g) * 2, 0) ^
+                            p.qsign;
+            qf[qb][s] = as<V8>(x);
+        }
+
+    // Direct loads (as in the 32x32 kernel): the wave's load i fills LDS chunks
+    // [(wave LOADS + i) 64, + 64); load i is load 0 moved by 1024 i bytes in
+    // memory and in LDS, with the chunk permutation changed by an XOR (checked
+    // above for this shape).
+    uint32_t koff0, voff0;
+    {
+        const int pch = wave * LOADS * 64 + lane;
+        const int row = pch / DC, col = pch % DC;
+        koff0 = row * ROWB + ((col ^ kswz<ROWB>(row)) << 4);
+        voff0 = row * ROWB + ((col ^ vswz16<D>(row)) << 4);
+    }
+    constexpr int kx1 = k16_xor<ROWB>(1), kx2 = k16_xor<ROWB>(2), kx3 = k16_xor<ROWB>(3);
+    constexpr int vx1 = v16_xor<D>(1), vx2 = v16_xor<D>(2), vx3 = v16_xor<D>(3);
+    auto issue = [&](const u32x4 &rsrc, uint32_t off0, auto x1, auto x2, auto x3, const u32x4 *dst_tile, int kb) {
+        const uint32_t tile = static_cast<uint32_t>(kb) * BN * ROWB;
+        const u32x4 *dst = dst_tile + wave * LOADS * 64;
+        dma_to_lds16<0>(rsrc, off0, tile, dst);
+        if constexpr (LOADS > 1) dma_to_lds16<1024>(rsrc, off0 ^ (decltype(x1)::value << 4), tile, dst);
+        if constexpr (LOADS > 2) dma_to_lds16<2048>(rsrc, off0 ^ (decltype(x2)::value << 4), tile, dst);
+        if constexpr (LOADS > 3) dma_to_lds16<3072>(rsrc, off0 ^ (decltype(x3)::value << 4), tile, dst);
+    };
+    auto issue_k = [&](auto st, int kb) {
+        issue(rk, koff0, IC<kx1>{}, IC<kx2>{}, IC<kx3>{}, sk[decltype(st)::value], kb);
+    };
+    auto issue_v = [&](auto st, int kb) {
+        issue(rv, voff0, IC<vx1>{}, IC<vx2>{}, IC<vx3>{}, sv[decltype(st)::value], kb);
+    };
+    // Step j requests V_{j+NS-1} and K_{j+NS}; at the end of step j, K_{j+2}
+    // and V_{j+1} must have landed.
+    auto allowance = [&](int j) {
+        int n = 0;
+#pragma unroll
+        for (int i = j + 3 - NS; i <= j; ++i)
+            if (i >= 1 - NS) n += LOADS * (i + NS - 1 < nkb) + LOADS * (i + NS < nkb);
+        return n;
+    };
+    constexpr int kMaxWait = 2 * (NS - 2);
+
+    // LDS byte offsets of this lane's operands within a tile.
+    // K (kb, s): row 16 kb + i, logical chunk 4 s + g; the permutation depends
+    // on i only, and chunk 4 s + g is chunk g XOR 4 s.
+    const uint32_t ka0 = li * ROWB + ((g ^ kswz<ROWB>(li)) << 4);
+    // V^T (db, s, h): the in-group lane i addresses row 4 g + i / 4 (+ 32 s +
+    // 16 h) and bytes 32 db + 8 (i % 4) .. + 7, so that lane i receives dims
+    // 16 db + i of the four rows; db enters as an XOR on the chunk index, and
+    // the row offsets leave the permutation unchanged.
+    uint32_t va0;
+    {
+        const int row = 4 * g + (li >> 2);
+        va0 = row * ROWB + ((((li & 3) >> 1) ^ vswz16<D>(row)) << 4) + ((li & 1) << 3);
+    }
+
+    f32x4 oacc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};  // reference maximum (base 2), per query block
+    float l_run[2] = {0.f, 0.f}, l_cmp[2] = {0.f, 0.f};
+    const float cs = p.c;
+
+    auto add_l = [&](int qb, float x) {
+        const float y = x - l_cmp[qb];
+        const float t = l_run[qb] + y;
+        l_cmp[qb] = (t - l_run[qb]) - y;
+        l_run[qb] = t;
+    };
+
+    using Frag = f32x4[4][2];  // [key block][query block]
+    // S^T = K Q^T for the K tile in stage st.
+    auto kop = [&](const char *SK, int s, int kb) {
+        return *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ ((4 * s) << 4)) + kb * 16 * ROWB);
+    };
+    auto scores = [&](auto st, Frag &sn) {
+        const char *SK = reinterpret_cast<const char *>(sk[decltype(st)::value]);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) sn[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const u32x4 x = kop(SK, s, kb);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) sn[kb][qb] = mfma16(as<V8>(x), qf[qb][s], sn[kb][qb]);
+            }
+    };
+
+    // A key is hidden from a query when key > min(query + off, Nkv - 1) (or
+    // past Nkv alone without the causal mask).  With t = that bound - kv0 - 4 g
+    // per query block, element (kb, r) is hidden iff 16 kb + r > t; the select
+    // is a bitfield insert on the sign of t - 16 kb - r, so no per-element
+    // compare result has to live in a scalar register pair.
+    auto needs_mask = [&](int kv0) { return (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off); };
+    auto mask = [&](Frag &sn, int kv0) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            int lim = p.Nkv - 1;
+            if constexpr (CAUSAL) lim = min(lim, wq0 + 16 * qb + li + off);
+            const int t = lim - kv0 - 4 * g;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                // whole-vector bit casts (a bit cast of one vector element is
+                // lowered as a read of element 0)
+                u32x4 bits = __builtin_bit_cast(u32x4, sn[kb][qb]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t hide = static_cast<uint32_t>((t - 16 * kb - r) >> 31);  // all ones when hidden
+                    bits[r] = (hide & 0xff800000u) | (~hide & bits[r]);
+                }
+                sn[kb][qb] = __builtin_bit_cast(f32x4, bits);
+            }
+        }
+    };
+
+    // P of tile sc against m_run, in the storage type: operand (qb, s) holds
+    // key blocks 2 s and 2 s + 1.  Returns this lane's sums over its keys:
+    // for fp16, of the rounded P that the second product takes, so that
+    // O = acc / l is a weighted mean whose weights sum to one exactly as
+    // rounded (each widened by v_fma_mix; v_dot2c would take half the
+    // instructions but shares the matrix pipeline and waits behind the other
+    // wave's MFMAs: measured 25 cycles each beside an MFMA stream, against 12
+    // for v_fma_mix); for bf16, of the fp32 values (widening a bf16 half
+    // costs an extra instruction, and the bf16 bar is eight times wider).
+    V8 pf[2][2];
+    auto probs = [&](const Frag &sc, float (&rs)[2]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float neg_m = -m_run[qb];
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 w;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4 v = sc[2 * s + h][qb];
+                    const float a = fast_exp2(fmaf(v[0], cs, neg_m)), b = fast_exp2(fmaf(v[1], cs, neg_m));
+                    const float c = fast_exp2(fmaf(v[2], cs, neg_m)), d = fast_exp2(fmaf(v[3], cs, neg_m));
+                    w[2 * h] = pack2<T>(a, b);
+                    w[2 * h + 1] = pack2<T>(c, d);
+                    if constexpr (std::is_same<T, _Float16>::value) {
+                        r0 = add_lo_f16(add_lo_f16(r0, w[2 * h]), w[2 * h + 1]);
+                        r1 = add_hi_f16(add_hi_f16(r1, w[2 * h]), w[2 * h + 1]);
+                    } else {
+                        r0 += a + c;
+                        r1 += b + d;
+                    }
+                }
+                pf[qb][s] = as<V8>(w);
+            }
+            rs[qb] = r0 + r1;
+        }
+    };
+    // The softmax step of tile sc, with the maximum taken on demand.
+    auto softmax = [&](const Frag &sc) {
+        float rs[2];
+        probs(sc, rs);
+        if (__builtin_amdgcn_ballot_w64(!(rs[0] <= kSumLimit && rs[1] <= kSumLimit))) {
+            // the four lanes of a query (i, i + 16, i + 32, i + 48) agree on
+            // the new reference: the tile's maximum across them, or m_run
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float m = sc[0][qb][0];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m = fmaxf(m, sc[kb][qb][r]);
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const float m_new = fmaxf(m_run[qb], m * cs);
+                // m_new is finite: the tile's first step of a row sees key 0,
+                // and m_run stays finite after it
+                const float alpha = fast_exp2(m_run[qb] - m_new);
+                l_run[qb] *= alpha;
+                l_cmp[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+                m_run[qb] = m_new;
+            }
+            probs(sc, rs);
+        }
+        add_l(0, rs[0]);
+        add_l(1, rs[1]);
+    };
+    auto pin = [](V8 (&pfr)[2][2]) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 w = __builtin_bit_cast(u32x4, pfr[qb][s]);
+                asm volatile("" : "+v"(w));
+                pfr[qb][s] = as<V8>(w);
+            }
+    };
+
+    // O^T += V^T P^T for the V tile in stage st.
+    auto vop = [&](const char *SV, int s, int db) {
+        const char *pa = SV + (va0 ^ (db << 5)) + 32 * s * ROWB;
+        const u32x2 lo = lds_read_tr16(pa);
+        const u32x2 hi = lds_read_tr16(pa + 16 * ROWB);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    auto pv = [&](auto st) {
+        const char *SV = reinterpret_cast<const char *>(sv[decltype(st)::value]);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 a = vop(SV, s, db);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) oacc[db][qb] = mfma16(as<V8>(a), pf[qb][s], oacc[db][qb]);
+            }
+    };
+
+    // Eight waves alternate MFMA and softmax blocks (below); other shapes
+    // overlap them within each wave.
+    constexpr bool kAlternate = NW == 8 && NS == 2;
+
+    // One pipeline step for key tile j (stage S = j % NS): V_j in sv[S],
+    // K_{j+1} in sk[(S + 1) % NS]; the two score sets alternate with j % 2.
+    Frag sa, sb;
+    auto step = [&](auto st, Frag &sc, Frag &sn, int j) {
+        constexpr int S = decltype(st)::value % NS;
+        if (j + NS - 1 < nkb) issue_v(IC<(S + NS - 1) % NS>{}, j + NS - 1);
+        if (j + NS < nkb) issue_k(IC<S>{}, j + NS);
+        if (j < nkw) {
+            // phase 1: MFMAs of the next scores beside the softmax of the current ones
+            scores(IC<(S + 1) % NS>{}, sn);
+            softmax(sc);
+            pin(pf);
+            const int kv1 = (j + 1) * BN;
+            if (needs_mask(kv1)) mask(sn, kv1);
+            // phase 2: MFMAs of O += V P
+            pv(IC<S>{});
+        }
+        wait_loads<LOADS, kMaxWait>(allowance(j));
+        __syncthreads();
+    };
+
+    if (nkb > 0) issue_k(IC<0>{}, 0);
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((I < nkb ? (issue_v(IC<I>{}, I), 0) : 0, I + 1 < nkb ? (issue_k(IC<I + 1>{}, I + 1), 0) : 0), ...);
+    }(std::make_integer_sequence<int, NS - 1>{});
+    wait_loads<LOADS, kMaxWait>(allowance(-1));
+    __syncthreads();
+    if (nkw > 0) {
+        scores(IC<0>{}, sa);
+        if (!kAlternate && needs_mask(0)) mask(sa, 0);
+    }
+    __syncthreads();  // every wave is done with sk[0] before K_NS refills it
+
+    if constexpr (kAlternate) {
+        // Alternating blocks.  Every wave runs the same sequence
+        //   M_j: S_{j+1} = K_{j+1} Q^T and O += V_j P_j (MFMA only),
+        //   V_{j+1}: softmax of S_{j+1} into P_{j+1} (VALU only),
+        // and the step's barrier falls after V for waves 0..3 and after M for
+        // waves 4..7, so that each SIMD starts a step with one wave on its
+        // MFMA block and the other on its softmax.  Between barriers j - 1 and
+        // j every wave runs M_j, so the ring protocol is the plain step's.
+        const bool lead = wave < NW / 2;
+        auto loads = [&](int j) __attribute__((always_inline)) {
+            const int S = j & 1;
+            if (j + 1 < nkb) issue(rv, voff0, IC<vx1>{}, IC<vx2>{}, IC<vx3>{}, sv[S ^ 1], j + 1);
+            if (j + 2 < nkb) issue(rk, koff0, IC<kx1>{}, IC<kx2>{}, IC<kx3>{}, sk[S], j + 2);
+        };
+        auto end_step = [&](int j) __attribute__((always_inline)) {
+            wait_loads<LOADS, kMaxWait>(allowance(j));
+            __syncthreads();
+        };
+        auto vblock = [&](int j) __attribute__((always_inline)) {
+            const int kv = j * BN;
+            if (needs_mask(kv)) mask(sa, kv);
+            softmax(sa);
+            pin(pf);
+        };
+        // M with its LDS operands requested ahead of the MFMAs that take
+        // them: K k-step s + 1 while k-step s multiplies (8 MFMAs, 128
+        // cycles), and the V operands kVAhead groups (2 MFMAs each) ahead.
+        constexpr int kVAhead = 6;
+        auto mblock = [&](auto st) __attribute__((always_inline)) {
+            constexpr int S = decltype(st)::value;
+            const char *SK = reinterpret_cast<const char *>(sk[S ^ 1]);
+            const char *SV = reinterpret_cast<const char *>(sv[S]);
+            constexpr int NG = 2 * DB;  // V groups: (s, db)
+            u32x4 kx[2][4], vx[kVAhead + 1];
+            auto kread = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) kx[s & 1][kb] = kop(SK, s, kb);
+            };
+            auto vread = [&](int gi) __attribute__((always_inline)) { vx[gi % (kVAhead + 1)] = vop(SV, gi / DB, gi % DB); };
+            kread(0);
+            if constexpr (KS > 1) kread(1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        sa[kb][qb] = mfma16(as<V8>(kx[s & 1][kb]), qf[qb][s],
+                                            s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sa[kb][qb]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + 2 < KS) kread(s + 2);
+                if (s == KS - 2 || (KS == 1 && s == 0)) {
+#pragma unroll
+                    for (int gi = 0; gi < kVAhead && gi < NG; ++gi) vread(gi);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const u32x4 a = vx[gi % (kVAhead + 1)];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    oacc[gi % DB][qb] = mfma16(as<V8>(a), pf[qb][gi / DB], oacc[gi % DB][qb]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (gi + kVAhead < NG) vread(gi + kVAhead);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // a step of a wave that has tile j + 1 after tile j
+        auto full = [&](auto st, int j) __attribute__((always_inline)) {
+            loads(j);
+            mblock(st);
+            if (!lead) end_step(j);
+            vblock(j + 1);
+            if (lead) end_step(j);
+        };
+        if (0 < nkw) vblock(0);
+        int j = 0;
+        for (; j + 2 < nkw; j += 2) {
+            full(IC<0>{}, j);
+            full(IC<1>{}, j + 1);
+        }
+        if (j + 1 < nkw) full(IC<0>{}, j++);
+        if (j < nkw) {  // the wave's last tile
+            loads(j);
+            if (j & 1)
+                pv(IC<1>{});
+            else
+                pv(IC<0>{});
+            end_step(j++);
+        }
+        for (; j < nkb; ++j) {  // tiles of the workgroup's later rows only
+            loads(j);
+            end_step(j);
+        }
+    } else {
+        for (int j = 0; j < nkb; j += U) {
+            [&]<int... I>(std::integer_sequence<int, I...>) {
+                ((j + I < nkb ? (I % 2 == 0 ? step(IC<I>{}, sa, sb, j + I) : step(IC<I>{}, sb, sa, j + I)), 0 : 0),
+                 ...);
+            }(std::make_integer_sequence<int, U>{});
+        }
+    }
+
+    // Epilogue: the four lanes' partial sums of a query, then O = acc / l and
+    // LSE = ln 2 (m + log2 l).
+    float inv[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float l = l_run[qb] - l_cmp[qb];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        inv[qb] = 1.f / l;
+        const int qrow = wq0 + 16 * qb + li;
+        if (g == 0 && p.lse && qrow < p.Nq)
+            p.lse[static_cast<size_t>(bh) * p.Nq + qrow] = (m_run[qb] + __builtin_amdgcn_logf(l)) * kLn2;
+    }
+    if constexpr (!OUT_F32) {
+        // 16-bit O leaves through LDS: the wave's 32 rows are written to its
+        // slice of the (now idle) ring, row-major with the 16-byte chunks of
+        // row r permuted by r mod (chunks per row), and read back so that
+        // every store writes whole rows (1 KB per instruction) rather than
+        // 32-byte pieces of 16 rows.  The loop's last barrier ended every
+        // wave's use of the ring and every load into it.
+        constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+        constexpr int RPI = 1024 / ROWB;  // rows per 1 KB instruction
+        static_assert(NW * 32 * ROWB <= static_cast<int>(sizeof(lds_rings)), "O stage fits the ring");
+        char *const stage = reinterpret_cast<char *>(lds_rings) + wave * 32 * ROWB;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = 16 * qb + li;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const f32x4 o = oacc[db][qb] * inv[qb];
+                const int byte = 32 * db + 8 * g;
+                *reinterpret_cast<u32x2 *>(stage + row * ROWB + ((((byte >> 4) ^ (row % CPR)) << 4) | (byte & 8))) =
+                    u32x2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
+            }
+        }
+        char *const obase = static_cast<char *>(p.o) + static_cast<size_t>(bh) * p.Nq * ROWB;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int row = i * RPI + lane / CPR, chunk = lane % CPR;
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(stage + row * ROWB + ((chunk ^ (row % CPR)) << 4));
+            if (wq0 + row < p.Nq)
+                *reinterpret_cast<u32x4 *>(obase + static_cast<size_t>(wq0 + row) * ROWB + chunk * 16) = x;
+        }
+    } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qrow = wq0 + 16 * qb + li;
+            if (qrow < p.Nq) {
+                const size_t orow = (static_cast<size_t>(bh) * p.Nq + qrow) * D;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int d0 = 16 * db + 4 * g;
+                    const f32x4 o = oacc[db][qb] * inv[qb];
+                    if constexpr (OUT_F32) {
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + orow + d0) = o;
+                    } else {
+                        *reinterpret_cast<u32x2 *>(static_cast<T *>(p.o) + orow + d0) =
+                            u32x2{pack2<T>(o[0], o[1]), pack2<T>(o[2], o[3])};
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Launch shapes: 8 waves (256 rows per workgroup, one workgroup per CU) when
 // the grid gives every CU such a workgroup; two 4-wave key groups on 128 rows
 // when even 128-row tiles leave CUs idle; else 4 waves (128 rows, two
@@ -670,12 +1232,38 @@ Shape pick_shape(const FwdArgs &a)
     return {4, 1};
 }
 
+// The 16x16x32 kernel for 16-bit K in the one-group shapes.
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW>
+hipError_t launch16(const FwdArgs &a, hipStream_t stream)
+{
+    constexpr int BM = 32 * NW;
+    FwdParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.o = a.o;
+    p.lse = a.lse;
+    p.Nq = a.Nq;
+    p.Nkv = a.Nkv;
+    p.n_bh = a.B * a.H;
+    p.n_qt = (a.Nq + BM - 1) / BM;
+    const float c = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
+    p.c = c < kMinC ? kMinC : c;
+    p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_qt));
+    hipLaunchKernelGGL((fwd16_kernel<D, T, CAUSAL, OUT_F32, NW, 2>), grid, dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+}
+
+// 16-bit K in the one-group shapes runs the 16x16x32 kernel; the two-group
+// shapes and E4M3 K run the 32x32x16 one.
 template <int D, typename T, bool CAUSAL, bool OUT_F32, bool KF8>
 hipError_t launch_k(const FwdArgs &a, hipStream_t stream)
 {
     const Shape s = pick_shape(a);
     if constexpr (!KF8)
-        if (s.nw == 8 && s.kg == 1) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8>(a, stream);
+        if (s.kg == 1) return s.nw == 8 ? launch16<D, T, CAUSAL, OUT_F32, 8>(a, stream)
+                                        : launch16<D, T, CAUSAL, OUT_F32, 4>(a, stream);
     if constexpr (CAUSAL && D == 64 && !KF8)
         if (s.nw == 4 && s.kg == 2) return launch_shape<D, T, CAUSAL, OUT_F32, 4, 2, KF8, 2>(a, stream);
     if (s.nw == 8 && s.kg == 2) return launch_shape<D, T, CAUSAL, OUT_F32, 8, 2, KF8, 2>(a, stream);
