@@ -129,27 +129,133 @@ def calibrate_copy():
 
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w, x, target_s=12.0):
-    """The oracle on a sample of the prefill heads: time one head, then enough to fill ~target_s."""
+ORACLE_BUDGET_S = 30.0   # CPU seconds of oracle work per leg (whole heads, at least one)
+TOL_O = {"f16": 2e-3, "bf16": 1.5e-2}  # max |O - O_oracle|, per input type
+TOL_LSE = 1e-3                         # max |LSE - LSE_oracle|
+TOL_GRAD_REL = {"f16": 10 * 2.0 ** -11, "bf16": 10 * 2.0 ** -8}  # backward: of max |grad_oracle|
+
+
+def host_info():
+    """The host CPU the oracle runs on: model name and logical cores."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cores": os.cpu_count()}
+
+
+class Worst:
+    """Largest |got - ref| over the elements added so far, with its index; any NaN fails."""
+
+    def __init__(self):
+        self.err, self.at, self.nan, self.n, self.abs_sum, self.ref_max = 0.0, None, False, 0, 0.0, 0.0
+
+    def add(self, got, ref, prefix=()):
+        import numpy as np
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        if got.size == 0:
+            return
+        self.nan |= bool(np.isnan(got).any())
+        diff = np.abs(got - ref)
+        k = int(np.nanargmax(diff)) if not np.isnan(diff).all() else 0
+        if diff.flat[k] > self.err or self.at is None:
+            self.err, self.at = float(diff.flat[k]), [*prefix, *(int(i) for i in np.unravel_index(k, diff.shape))]
+        self.n += got.size
+        self.abs_sum += float(np.nansum(diff))
+        self.ref_max = max(self.ref_max, float(np.max(np.abs(ref))))
+
+    def record(self, name, tol=None, rel=None):
+        out = {f"err_{name}": self.err, f"worst_{name}": self.at, f"mean_abs_err_{name}": self.abs_sum / max(self.n, 1)}
+        if rel is not None:
+            out[f"err_{name}_rel"] = self.err / self.ref_max if self.ref_max else 0.0
+        ok = not self.nan and (tol is None or self.err <= tol) and (rel is None or self.err <= rel * self.ref_max)
+        return out, ok
+
+
+def oracle_forward_leg(w, head_inputs, o_dev, lse_dev, budget_s=ORACLE_BUDGET_S, fp8=False, keep_ref=False):
+    """The oracle beside one forward leg.
+
+    Whole heads of workload w, one at a time (head_inputs(b, h) -> the head's
+    q, k, v bits), until budget_s of oracle time has passed: the time gives
+    the leg's cpu_baseline, and the results are compared with every element
+    of the same heads of the outputs the timed calls produced (o_dev, lse_dev,
+    as timed: O in the input type).  keep_ref also returns the oracle's O
+    rounded to the input type and its LSE for every head it ran."""
+    import numpy as np
+
+    import fa_inputs as fi
     import oracle
-    heads = 0
-    t0 = time.perf_counter()
-    while heads < w.heads:
-        b, h = divmod(heads, w.H)
-        oracle.attention(x["q"][b, h], x["k"][b, h], x["v"][b, h], causal=w.causal, scale=w.scale,
-                         dtype=w.dtype)
+    o_all = o_dev.float().cpu().numpy()
+    lse_all = lse_dev.float().cpu().numpy().reshape(o_all.shape[:3])
+    wo, wl = Worst(), Worst()
+    spent, heads, kept = 0.0, 0, {}
+    for bh in range(w.heads):
+        b, h = divmod(bh, w.H)
+        q, k, v = head_inputs(b, h)
+        t0 = time.perf_counter()
+        if fp8:
+            o_ref, lse_ref = oracle.attention_fp8qk(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype)
+        else:
+            o_ref, lse_ref = oracle.attention(q, k, v, causal=w.causal, scale=w.scale, dtype=w.dtype)
+        spent += time.perf_counter() - t0
         heads += 1
-        if time.perf_counter() - t0 >= target_s:
+        wo.add(o_all[b, h], o_ref, (b, h))
+        wl.add(lse_all[b, h], lse_ref, (b, h))
+        if keep_ref:
+            kept[(b, h)] = (fi.f32_to_bits(o_ref.astype(np.float32), w.dtype), lse_ref.astype(np.float32))
+        if spent >= budget_s:
             break
-    dt = time.perf_counter() - t0
     flops = metric_flops(1, heads, w.Nq, w.Nkv, w.d, w.causal)
-    return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": oracle.threads(),
-        "kind": "oracle",
-        "sample": f"{heads} of {w.heads} heads of {w.name} (fp64, score matrix materialised), {dt:.1f} s",
-    }
+    ro, ok_o = wo.record("O", TOL_O[w.dtype])
+    rl, ok_l = wl.record("LSE", TOL_LSE)
+    cpu = {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+           "seconds": round(spent, 2),
+           "sample": f"{heads} of {w.heads} heads of {w.name} ({'E4M3 Q and K, ' if fp8 else ''}fp64, score "
+                     f"matrix materialised), {spent:.1f} s"}
+    parity = {**ro, **rl, "tol_O": TOL_O[w.dtype], "tol_LSE": TOL_LSE, "pass": ok_o and ok_l,
+              "compared": f"every element of O ({w.dtype}, as timed) and LSE of {heads} of {w.heads} heads",
+              "index": "worst_O = [b, h, row, dim], worst_LSE = [b, h, row]"}
+    return (cpu, parity, kept) if keep_ref else (cpu, parity)
+
+
+def oracle_decode_leg(w, head_inputs, o_dev, lse_dev, budget_s=ORACLE_BUDGET_S):
+    """The oracle beside decode: heads of workload w, one at a time
+    (head_inputs(b, h) -> the head's q [1, d], k, v bits), until budget_s of
+    oracle time has passed; compared with the timed calls' O (input type) and
+    LSE."""
+    import oracle
+    o_all = o_dev.float().cpu().numpy().reshape(w.B, w.H, w.d)
+    lse_all = lse_dev.float().cpu().numpy().reshape(w.B, w.H)
+    wo, wl = Worst(), Worst()
+    spent, heads = 0.0, 0
+    for bh in range(w.heads):
+        b, h = divmod(bh, w.H)
+        q, k, v = head_inputs(b, h)
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attention(q, k, v, causal=False, scale=w.scale, dtype=w.dtype)
+        spent += time.perf_counter() - t0
+        heads += 1
+        wo.add(o_all[b, h], o_ref[0], (b, h))
+        wl.add(lse_all[b, h], lse_ref[0], (b, h))
+        if spent >= budget_s:
+            break
+    nbytes = algorithmic_bytes(1, heads, 1, w.Nkv, w.d)
+    ro, ok_o = wo.record("O", TOL_O[w.dtype])
+    rl, ok_l = wl.record("LSE", TOL_LSE)
+    cpu = {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+           "seconds": round(spent, 2),
+           "sample": f"{heads} of {w.heads} heads of {w.name} (fp64), {spent:.1f} s; rate over the same "
+                     f"algorithmic bytes as the GPU figure"}
+    parity = {**ro, **rl, "tol_O": TOL_O[w.dtype], "tol_LSE": TOL_LSE, "pass": ok_o and ok_l,
+              "compared": f"O ({w.dtype}, as timed) and LSE of {heads} of {w.heads} heads",
+              "index": "worst_O = [b, h, dim], worst_LSE = [b, h]"}
+    return cpu, parity
 
 
 def backward_flops(B, H, Nq, Nkv, d, causal):
@@ -162,13 +268,24 @@ def backward_bytes(B, H, Nq, Nkv, d, elt=2):
     return B * H * (elt * (3 * Nq + 2 * Nkv) * d + 4 * Nq + elt * (Nq + 2 * Nkv) * d)
 
 
-def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
-    """fa_bwd on workload w (dO from the seeded generator), each call bracketed by HIP events."""
+def time_backward(fa, fi, w, q, k, v, stream, warmup, steps, fwd_ref=None, oracle_budget=None):
+    """fa_bwd on workload w (dO from the seeded generator), each call bracketed by HIP events.
+
+    fa_bwd is handed O (input type) and LSE: the oracle's for the heads in
+    fwd_ref ({(b, h): (O bits, LSE fp32)}), the GPU forward's for the rest.
+    With oracle_budget, the oracle's gradients (D from the same O) of the
+    fwd_ref heads, in order, until that many seconds have passed, are compared
+    with every element of those heads of the timed calls' dQ, dK, dV, and
+    the oracle's time is this leg's cpu_baseline."""
     import statistics
 
     import torch
-    dout = fi.bits_to_torch(fi.make_tensor(w, fi.DOUT), w.dtype).to(q.device)
+    dout_bits = fi.make_tensor(w, fi.DOUT)
+    dout = fi.bits_to_torch(dout_bits, w.dtype).to(q.device)
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    for (b, h), (o16, l32) in (fwd_ref or {}).items():
+        o[b, h] = fi.bits_to_torch(o16, w.dtype).to(q.device)
+        lse[b, h] = torch.from_numpy(l32).to(q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = fa.fa_bwd_workspace_size(w.B, w.H, w.Nq)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -190,7 +307,7 @@ def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
     ms = [a.elapsed_time(b) for a, b in evs]
     mean = statistics.fmean(ms)
     flops = backward_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
-    return {
+    res = {
         "workload": w.name,
         "ms_mean": round(mean, 4),
         "ms_min": round(min(ms), 4),
@@ -203,11 +320,45 @@ def time_backward(fa, fi, w, q, k, v, stream, warmup, steps):
         "note": "FLOPs counted as 2.5 x the forward (five products); the kernels do seven "
                 "(S and dP are formed in both the key-block and the query-block pass)",
     }
+    if oracle_budget and fwd_ref:
+        import oracle
+        got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+        worst = {n: Worst() for n in ("dQ", "dK", "dV")}
+        spent, heads = 0.0, 0
+        x = {t: fi.make_tensor(w, i) for t, i in (("q", fi.Q), ("k", fi.K), ("v", fi.V))}
+        for (b, h), (o16, _) in sorted(fwd_ref.items()):
+            t0 = time.perf_counter()
+            ref = oracle.attention_bwd(x["q"][b, h], x["k"][b, h], x["v"][b, h], dout_bits[b, h], causal=w.causal,
+                                       scale=w.scale, dtype=w.dtype, o_for_d=o16)
+            spent += time.perf_counter() - t0
+            heads += 1
+            for n, g, r in zip(("dQ", "dK", "dV"), got, ref):
+                worst[n].add(g[b, h], r, (b, h))
+            if spent >= oracle_budget:
+                break
+        parity, ok = {}, True
+        for n, wst in worst.items():
+            rec, good = wst.record(n, rel=TOL_GRAD_REL[w.dtype])
+            parity.update(rec)
+            ok &= good
+        parity.update({"tol_rel": TOL_GRAD_REL[w.dtype], "pass": ok,
+                       "compared": f"every element of dQ, dK, dV ({w.dtype}, as timed) of {heads} of {w.heads} "
+                                   "heads; fa_bwd handed the oracle's O (rounded to the input type) and LSE for "
+                                   "them, and the oracle forms D from the same O",
+                       "index": "worst_* = [b, h, row, dim]"})
+        res["parity"] = parity
+        res["cpu_baseline"] = {"value": flops / w.heads * heads / spent / 1e12, "unit": "TFLOP/s",
+                               "cores": oracle.threads(), "kind": "oracle", "seconds": round(spent, 2),
+                               "sample": f"{heads} of {w.heads} heads of {w.name}, the backward (fp64, P and dS "
+                                         f"materialised), {spent:.1f} s"}
+    return res
 
 
-def time_fp8_forward(fa, fi, w, q, k, v, stream, warmup, steps):
+def time_fp8_forward(fa, fi, w, q, k, v, stream, warmup, steps, head_inputs=None, oracle_budget=ORACLE_BUDGET_S):
     """fa_fwd_fp8 on workload w: K rounded to E4M3 once (timed on its own), then
-    the forward with Q rounded in the kernel, each call bracketed by HIP events."""
+    the forward with Q rounded in the kernel, each call bracketed by HIP events.
+    With head_inputs (b, h -> the head's 16-bit q, k, v bits) the oracle of
+    the FP8 variant (its own E4M3 codec on q and k) runs beside it."""
     import statistics
 
     import torch
@@ -238,6 +389,9 @@ def time_fp8_forward(fa, fi, w, q, k, v, stream, warmup, steps):
     qms = timed(quant)
     ms = timed(call)
     mean = statistics.fmean(ms)
+    oracle_leg = None
+    if head_inputs is not None:
+        oracle_leg = oracle_forward_leg(w, head_inputs, o, lse, budget_s=oracle_budget, fp8=True)
     flops = metric_flops(w.B, w.H, w.Nq, w.Nkv, w.d, w.causal)
     tflops = flops / (mean * 1e-3) / 1e12
     # half the FLOPs (Q K^T) at the E4M3 rate, half (P V) at the 16-bit rate
@@ -254,6 +408,7 @@ def time_fp8_forward(fa, fi, w, q, k, v, stream, warmup, steps):
         "traffic": measured_traffic("prefill", "fp8"),
         "note": "Q K^T on the E4M3 MFMA (5.0 PFLOP/s peak), P V in 16 bits (2.5 PFLOP/s); K rounded to E4M3 once "
                 "before the timed calls (quantize_k_ms), Q inside the kernel",
+        **({"cpu_baseline": oracle_leg[0], "parity": oracle_leg[1]} if oracle_leg else {}),
     }
 
 
@@ -653,8 +808,9 @@ def run_data_probe(warmup, steps, rounds=6):
 OTHER_PREFILL = ("prefill_2k_d64", "prefill_16k_d128_bf16")
 
 
-def time_other_prefill(fa, fi, names, dev, stream, warmup, steps):
-    """fa_fwd on the other prefill workloads (reported beside the headline one, not part of `value`)."""
+def time_other_prefill(fa, fi, names, dev, stream, warmup, steps, oracle_budget=None):
+    """fa_fwd on the other prefill workloads (reported beside the headline one, not part of `value`);
+    with oracle_budget the oracle runs beside each (cpu_baseline and parity of the timed outputs)."""
     import torch
     sp = stream.cuda_stream
     res = []
@@ -662,7 +818,6 @@ def time_other_prefill(fa, fi, names, dev, stream, warmup, steps):
         w = fi.WORKLOADS[name]
         x = fi.make_inputs(w)
         q, k, v = (fi.bits_to_torch(x[t], w.dtype).to(dev) for t in "qkv")
-        x = None
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
         code = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
@@ -681,13 +836,70 @@ def time_other_prefill(fa, fi, names, dev, stream, warmup, steps):
                     "note": "ms_mean: each call between its own HIP events (includes the host's launch gap for "
                             "short calls); ms_graph: the same calls captured once into a HIP graph and replayed "
                             "back to back"})
-        q = k = v = o = lse = None
+        if oracle_budget:
+            cpu, parity = oracle_forward_leg(w, lambda b, h: (x["q"][b, h], x["k"][b, h], x["v"][b, h]), o, lse,
+                                             budget_s=oracle_budget)
+            res[-1]["cpu_baseline"], res[-1]["parity"] = cpu, parity
+        q = k = v = o = lse = x = None
     return res
 
 
-def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
+def oracle_paged_leg(w, plan, q, kp, vp, o, lse, budget_s):
+    """The oracle beside the paged decode leg: whole sequences, one at a time,
+    each over the pool pages its table names (copied back from wherever the
+    pool lives, with the table renumbered to them), until budget_s seconds of
+    oracle time have passed.  q and o are [B, H, 1, d] (o as timed, in the
+    input type), lse [B, H], kp / vp the 'hnd' pool [P, H, ps, d].  Returns
+    the parity record and the cpu_baseline."""
+    import time
+
+    import numpy as np
+    import torch
+
+    import fa_inputs as fi
+    import oracle
+    o_all = o.float().cpu().numpy().reshape(w.B, w.H, w.d)
+    lse_all = lse.float().cpu().numpy().reshape(w.B, w.H)
+    wo, wl = Worst(), Worst()
+    spent, seqs, seq_keys = 0.0, 0, 0
+    for b in range(w.B):
+        n = int(plan.seq_lens[b])
+        pages = plan.block_table[b, :-(-n // plan.page_size)].astype(np.int64)
+        idx = torch.from_numpy(pages).to(kp.device)
+        kb, vb = (fi.torch_to_bits(t[idx].cpu()) for t in (kp, vp))
+        qb = fi.torch_to_bits(q[b:b + 1].reshape(1, w.H, w.d).cpu())
+        table_b = np.arange(len(pages), dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.paged_decode(qb, kb, vb, table_b, np.array([n], dtype=np.int32), scale=w.scale,
+                                             layout="hnd", dtype=w.dtype)
+        spent += time.perf_counter() - t0
+        seqs += 1
+        seq_keys += n
+        wo.add(o_all[b], o_ref[0], (b,))
+        wl.add(lse_all[b], lse_ref[0], (b,))
+        if spent >= budget_s:
+            break
+    ro, ok_o = wo.record("O", TOL_O[w.dtype])
+    rl, ok_l = wl.record("LSE", TOL_LSE)
+    sample_bytes = 2 * seq_keys * w.H * w.d * 2 + algorithmic_bytes(1, seqs * w.H, 1, 0, w.d)
+    return {
+        "parity": {**ro, **rl, "tol_O": TOL_O[w.dtype], "tol_LSE": TOL_LSE, "pass": ok_o and ok_l,
+                   "compared": f"O ({w.dtype}, as timed) and LSE of {seqs} of {w.B} sequences (all heads)",
+                   "index": "worst_O = [b, h, dim], worst_LSE = [b, h]"},
+        "cpu_baseline": {"value": sample_bytes / max(spent, 1e-9) / 1e9, "unit": "GB/s", "cores": oracle.threads(),
+                         "kind": "oracle", "seconds": round(spent, 2),
+                         "sample": f"{seqs} of {w.B} sequences of {w.name} through the oracle's paged "
+                                   f"gather (fp64), {spent:.1f} s"},
+    }
+
+
+def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits, dense_o=None, oracle_budget=None):
     """fa_decode_paged on workload w: the dense decode cache k, v scattered into a
-    shuffled page pool, each call bracketed by HIP events."""
+    shuffled page pool, each call bracketed by HIP events.  dense_o (fa_decode's
+    output on the dense cache) is compared bit for bit; with oracle_budget the
+    oracle's paged decode runs on whole sequences (each over the pool pages its
+    table names, copied back from the device, with the table renumbered to
+    them) until that many seconds have passed."""
     import statistics
 
     import numpy as np
@@ -722,6 +934,11 @@ def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
     nbytes_alg = 2 * keys * w.H * w.d * 2 + algorithmic_bytes(w.B, w.H, 1, 0, w.d) + plan.block_table.nbytes + \
         plan.seq_lens.nbytes
     gbs = nbytes_alg / (mean * 1e-3) / 1e9
+    extra = {}
+    if dense_o is not None:
+        extra["bitwise_equal_to_dense_decode"] = bool(torch.equal(o, dense_o))
+    if oracle_budget:
+        extra.update(oracle_paged_leg(w, plan, q, kp, vp, o, lse, oracle_budget))
     return {
         "workload": w.name,
         "page_size": plan.page_size,
@@ -735,6 +952,7 @@ def time_paged_decode(fa, fi, w, q, k, v, stream, warmup, steps, num_splits):
         "traffic": measured_traffic("decode", "paged"),
         "note": "the dense decode cache scattered into a shuffled pool of 16-key pages; bytes are K and V "
                 "once, q, o, lse, the block table and the lengths",
+        **extra,
     }
 
 
@@ -809,8 +1027,9 @@ def main():
 
     run_prefill = args.only in ("all", "prefill")
     run_decode = args.only in ("all", "decode")
-    px = None
-    if run_prefill or not args.no_cpu_baseline:
+    oracle_on = not args.no_cpu_baseline
+    px = dx = None
+    if run_prefill:
         log(f"generating {PREFILL}")
         px = fi.make_inputs(pw)
     if run_prefill:
@@ -824,7 +1043,8 @@ def main():
         log(f"generating {DECODE}")
         dx = fi.make_inputs(dw)
         dq, dk, dv = (fi.bits_to_torch(dx[t], dw.dtype).to(dev) for t in "qkv")
-        dx = None  # decode inputs are not needed on the host any more
+        if not oracle_on:
+            dx = None  # the host copy only serves the oracle
         do = torch.empty_like(dq)
         dlse = torch.empty((dw.B, dw.H), dtype=torch.float32, device=dev)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -921,15 +1141,36 @@ def main():
         "sources": {"prefill_digest": kernel_source_digest("prefill"),
                     "decode_digest": kernel_source_digest("decode")},
     }
+    budget = ORACLE_BUDGET_S if oracle_on else None
+    fwd_ref = None
+    if oracle_on:
+        result["host"] = host_info()
+    if oracle_on and run_prefill:
+        log("oracle beside the prefill leg (cpu baseline, parity of the timed outputs)")
+        cpu, parity, fwd_ref = oracle_forward_leg(pw, lambda b, h: (px["q"][b, h], px["k"][b, h], px["v"][b, h]),
+                                                  po, plse, keep_ref=True)
+        result["cpu_baseline"] = cpu
+        result["prefill"]["parity"] = parity
+    if oracle_on and run_decode:
+        log("oracle beside the decode leg")
+        cpu, parity = oracle_decode_leg(dw, lambda b, h: (dx["q"][b, h], dx["k"][b, h], dx["v"][b, h]), do, dlse)
+        result["decode"]["cpu_baseline"], result["decode"]["parity"] = cpu, parity
+        if not run_prefill:
+            result["cpu_baseline"] = cpu
+        dx = None
     if run_prefill and not args.no_bwd:
         log("backward (fa_bwd) on the prefill workload")
-        result["backward"] = time_backward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
+        result["backward"] = time_backward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps, fwd_ref=fwd_ref,
+                                           oracle_budget=budget)
     if run_prefill and not args.no_other:
         log("other prefill workloads (fa_fwd)")
-        result["other_prefill"] = time_other_prefill(fa, fi, OTHER_PREFILL, dev, stream, args.warmup, args.steps)
+        result["other_prefill"] = time_other_prefill(fa, fi, OTHER_PREFILL, dev, stream, args.warmup, args.steps,
+                                                     oracle_budget=budget)
     if run_prefill and not args.no_fp8:
         log("FP8 Q/K forward (fa_fwd_fp8) on the prefill workload")
-        result["fp8_forward"] = time_fp8_forward(fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps)
+        result["fp8_forward"] = time_fp8_forward(
+            fa, fi, pw, pq, pk, pv, stream, args.warmup, args.steps,
+            head_inputs=(lambda b, h: (px["q"][b, h], px["k"][b, h], px["v"][b, h])) if oracle_on else None)
     if run_decode:
         log("streaming-read probe over the decode K cache")
         probe = measure_read_bandwidth(dk, stream, args.warmup, args.steps)
@@ -938,12 +1179,9 @@ def main():
     if run_decode and not args.no_paged:
         log("decode over a paged cache (fa_decode_paged)")
         result["paged_decode"] = time_paged_decode(fa, fi, fi.WORKLOADS[PAGED], dq, dk, dv, stream, args.warmup,
-                                                   args.steps, args.num_splits)
+                                                   args.steps, args.num_splits, dense_o=do, oracle_budget=budget)
     if args.only != "all":
         result["partial_step"] = args.only
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(pw, px)
     print(json.dumps(result), flush=True)
 
 

@@ -60,3 +60,53 @@ def test_comparator_fails_on_one_bad_element():
         o[0, 0, 0, 0] = np.nan
         with pytest.raises(AssertionError):
             check(o, lse_ref, o_ref, lse_ref, dtype, "NaN")
+
+
+def test_bench_comparator_names_the_worst_element():
+    # the bench's record of the timed outputs: the worst element's index across
+    # heads added one at a time, pass/fail at the stated tolerance, NaN fails,
+    # and the relative form used for the backward's gradients
+    rng = np.random.default_rng(6)
+    ref = rng.standard_normal((4, 5, 3))
+    w = bench.Worst()
+    for h in range(4):
+        got = ref[h].copy()
+        if h == 2:
+            got[3, 1] += 0.5
+        w.add(got, ref[h], (0, h))
+    rec, ok = w.record("O", tol=0.1)
+    assert rec["err_O"] == pytest.approx(0.5) and rec["worst_O"] == [0, 2, 3, 1] and not ok
+    assert w.record("O", tol=1.0)[1]
+    rec, ok = w.record("O", rel=0.5 / np.max(np.abs(ref)) * 1.01)
+    assert ok and rec["err_O_rel"] == pytest.approx(0.5 / np.max(np.abs(ref)))
+    w.add(np.array([np.nan]), np.array([0.0]), (9,))
+    assert not w.record("O", tol=1e9)[1]
+
+
+def test_bench_paged_oracle_leg_compares_each_sequence():
+    # the paged decode leg's oracle comparison on host tensors: each sequence
+    # through the oracle over the pool pages its table names (renumbered), the
+    # timed O taken as [B, H, 1, d]; a planted error is found at its index
+    import types
+
+    import torch
+
+    import fa_inputs as fi
+    import oracle
+    w = types.SimpleNamespace(B=3, H=2, d=64, dtype="f16", scale=0.125, name="paged_tiny")
+    plan = fi.paged_plan(5, w.B, 40, 16, ragged=True)
+    g = torch.Generator().manual_seed(8)
+    kp = torch.randn((plan.num_pages, w.H, plan.page_size, w.d), generator=g).half()
+    vp = torch.randn((plan.num_pages, w.H, plan.page_size, w.d), generator=g).half()
+    q = torch.randn((w.B, w.H, 1, w.d), generator=g).half()
+    o_ref, lse_ref = oracle.paged_decode(fi.torch_to_bits(q.reshape(w.B, w.H, w.d)), fi.torch_to_bits(kp),
+                                         fi.torch_to_bits(vp), plan.block_table, plan.seq_lens, scale=w.scale,
+                                         layout="hnd", dtype="f16")
+    o = torch.from_numpy(o_ref).half().reshape(w.B, w.H, 1, w.d)
+    lse = torch.from_numpy(lse_ref).float()
+    rec = bench.oracle_paged_leg(w, plan, q, kp, vp, o, lse, 100.0)
+    assert rec["parity"]["pass"] and rec["parity"]["err_O"] <= 2.0 ** -11
+    assert rec["cpu_baseline"]["kind"] == "oracle" and "3 of 3 sequences" in rec["cpu_baseline"]["sample"]
+    o[1, 1, 0, 5] += 0.5
+    rec = bench.oracle_paged_leg(w, plan, q, kp, vp, o, lse, 100.0)
+    assert not rec["parity"]["pass"] and rec["parity"]["worst_O"] == [1, 1, 5]
