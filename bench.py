@@ -1112,7 +1112,7 @@ def main():
                        "seed": dw.seed, "num_splits": splits},
         },
         "roofline": {
-            "kernel": "fwd_kernel<128, f16, causal>",
+            "kernel": "fwd16_kernel<128, f16, causal, 8 waves>",
             "bound": "mfma",
             "achieved": round(tflops, 2),
             "peak": PEAK_MFMA_F16_TFLOPS,
