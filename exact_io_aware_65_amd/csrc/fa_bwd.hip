@@ -173,7 +173,7 @@ void bwd_dkdv_kernel(BwdParams p)
     // permuted by kswz of its row; the lane then reads row 32 wave + c, logical
     // chunk 2 s + h, conflict-free as the forward's K reads.
     V8 kf[KS], vf[VLDS ? 1 : KS];
-    uint32_t va0 = 0;
+    uint32_t va0_ = 0;
     {
         const auto rk = make_rsrc(static_cast<const char *>(p.k) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
         const auto rv = make_rsrc(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
@@ -189,7 +189,7 @@ void bwd_dkdv_kernel(BwdParams p)
                 sv[row * DC + (col ^ kswz<D>(row))] = buffer_load16(rv, static_cast<uint32_t>(k0 + row) * ROWB + col * 16, 0);
             }
             const int vrow = 32 * wave + c;
-            va0 = vrow * ROWB + ((h ^ kswz<D>(vrow)) << 4);
+            va0_ = vrow * ROWB + ((h ^ kswz<D>(vrow)) << 4);
         }
     }
     const char *SV = reinterpret_cast<const char *>(sv);
@@ -214,22 +214,22 @@ void bwd_dkdv_kernel(BwdParams p)
 
     // Row reads of Q and dO (A operands of S and dP): row swap23(c) (+ 32 per
     // sub-tile), logical chunk 2 s + h.
-    uint32_t ra0;
+    uint32_t ra0_;
     {
         const int r = swap23(c);
-        ra0 = r * ROWB + ((h ^ dswz<D>(r)) << 4);
+        ra0_ = r * ROWB + ((h ^ dswz<D>(r)) << 4);
     }
     // Transposed reads (A operands of dV^T = dO^T P and dK^T = Q^T dS): lane
     // 16 g + 4 j + q addresses query 8 (g / 2) + j + 4 half (+ 16 u + 32 per
     // sub-tile) and dims 32 dt + 16 (g % 2) + 4 q .. + 3.  The permutation
     // depends on half; dt enters as an XOR on bits 6.. of the offset.
-    uint32_t ta0[2];
+    uint32_t ta0_[2];
     {
         const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int r = 8 * (g >> 1) + j + 4 * half;
-            ta0[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
+            ta0_[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
         }
     }
 
@@ -240,12 +240,37 @@ void bwd_dkdv_kernel(BwdParams p)
         for (int e = 0; e < 16; ++e) dvacc[dt][e] = dkacc[dt][e] = 0.f;
     const float cs = p.c;
 
-    auto subtile = [&](int st, int t, int qq) {
+    auto subtile = [&](auto stc, int t, int qq) {
+        constexpr int st = decltype(stc)::value;
         const char *SQ = reinterpret_cast<const char *>(sq[st]);
         const char *SDO = reinterpret_cast<const char *>(sdo[st]);
+        // the lane's base offsets, re-derived per sub-tile (kept opaque so that
+        // the per-k-step variants are formed here rather than held across the loop)
+        uint32_t ra0 = ra0_, ta0[2] = {ta0_[0], ta0_[1]}, va0 = va0_;
+        asm volatile("" : "+v"(ra0), "+v"(ta0[0]), "+v"(ta0[1]), "+v"(va0));
         const int qs0 = t * BQ + 32 * qq;  // first query of the sub-tile
         // S = Q K^T and dP = dO V^T (rows: queries in swap23 order; columns: keys)
         f32x16 s = {}, dp = {};
+        // Causal: hidden pairs start the S accumulation at -inf, so that the
+        // product leaves s = -inf and p = 2^(c s - l2) = 0.  Only sub-tiles
+        // that cross the diagonal or the ragged end take this; the common path
+        // has no per-score test.  Element e is query qs0 + 8 h + r(e), r(e) =
+        // 16 (e / 8) + e % 8, visible iff lo <= r(e) < hi.
+        // Without the causal mask the only hidden rows are those past Nq, and
+        // they need no test: their Q, dO, l2 and D are read as zeros, so p = 1
+        // there but dO = 0 and dS = p (dP - D) = 0, and they add nothing to
+        // dV or dK.
+        if constexpr (CAUSAL) {
+            if (qs0 + 32 > p.Nq || kw0 + 31 > qs0 + off) {
+                const int base = qs0 + 8 * h;
+                const int lo = key - off - base;
+                const int hi = max(p.Nq - base, lo);
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (static_cast<unsigned>(16 * (e / 8) + e % 8 - lo) >= static_cast<unsigned>(hi - lo))
+                        s[e] = -INFINITY;
+            }
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const uint32_t a = (ra0 ^ (ks << 5)) + qq * 32 * ROWB;
@@ -262,7 +287,6 @@ void bwd_dkdv_kernel(BwdParams p)
         const f32x4 *ddv = reinterpret_cast<const f32x4 *>(&sdd[st][32 * qq + 8 * h]);
         const f32x4 l2a[4] = {l2v[0], l2v[1], l2v[4], l2v[5]};
         const f32x4 dda[4] = {ddv[0], ddv[1], ddv[4], ddv[5]};
-        const bool edge = qs0 + 32 > p.Nq || (CAUSAL && kw0 + 31 > qs0 + off);
         u32x4 pw[2], dw[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -273,11 +297,7 @@ void bwd_dkdv_kernel(BwdParams p)
                 for (int b = 0; b < 2; ++b) {
                     const int e = 8 * u + 2 * j + b;
                     const float l2 = l2a[e / 4][e % 4], dd = dda[e / 4][e % 4];
-                    float pe = fast_exp2(fmaf(s[e], cs, -l2));
-                    if (edge) {
-                        const int qi = qs0 + 16 * u + 8 * h + 2 * j + b;
-                        if (qi >= p.Nq || (CAUSAL && key > qi + off)) pe = 0.f;
-                    }
+                    const float pe = fast_exp2(fmaf(s[e], cs, -l2));
                     pr[b] = pe;
                     dr[b] = pe * (dp[e] - dd);
                 }
@@ -298,9 +318,10 @@ void bwd_dkdv_kernel(BwdParams p)
             }
     };
 
-    if (t0 < nqt) issue(0, t0);
-    for (int t = t0; t < nqt; ++t) {
-        const int st = (t - t0) & 1;
+    // tile t sits in stage (t - t0) & 1; the loop takes two tiles per pass so
+    // that the stage is a constant of each copy
+    auto step = [&](auto stc, int t) {
+        constexpr int st = decltype(stc)::value;
         wait_vmcnt<0>();
         __syncthreads();  // tile t visible to every wave; tile t - 1's stage free
         if (t + 1 < nqt) issue(st ^ 1, t + 1);
@@ -308,8 +329,13 @@ void bwd_dkdv_kernel(BwdParams p)
         for (int qq = 0; qq < NQQ; ++qq) {
             const int qs0 = t * BQ + 32 * qq;
             // some (query, key) pair of the sub-tile is visible to this wave
-            if (qs0 < p.Nq && (!CAUSAL || qs0 + 31 >= wfirst)) subtile(st, t, qq);
+            if (qs0 < p.Nq && (!CAUSAL || qs0 + 31 >= wfirst)) subtile(stc, t, qq);
         }
+    };
+    if (t0 < nqt) issue(0, t0);
+    for (int t = t0; t < nqt; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
     }
 
     // Epilogue: lane (c, h) writes key kw0 + c, dims 32 dt + 8 j + 4 h .. + 3.
@@ -406,20 +432,20 @@ void bwd_dq_kernel(BwdParams p)
     };
 
     // Row reads of K (dswz) and V (kswz): row 32 kk + swap23(c), chunk 2 s + h.
-    uint32_t ka0, va0;
+    uint32_t ka0_, va0_;
     {
         const int r = swap23(c);
-        ka0 = r * ROWB + ((h ^ dswz<D>(r)) << 4);
-        va0 = r * ROWB + ((h ^ kswz<D>(r)) << 4);
+        ka0_ = r * ROWB + ((h ^ dswz<D>(r)) << 4);
+        va0_ = r * ROWB + ((h ^ kswz<D>(r)) << 4);
     }
     // Transposed reads of K (A operand of dQ^T = K^T dS^T), as in the dK/dV kernel.
-    uint32_t ta0[2];
+    uint32_t ta0_[2];
     {
         const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int r = 8 * (g >> 1) + j + 4 * half;
-            ta0[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
+            ta0_[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
         }
     }
 
@@ -432,9 +458,13 @@ void bwd_dq_kernel(BwdParams p)
 
     // One 64-key tile, as two 32-key halves each taken through S, dP, dS and
     // its dQ products before the next (half the score registers live at once).
-    auto tile = [&](int st, int kv0) {
+    auto tile = [&](auto stc, int kv0) {
+        constexpr int st = decltype(stc)::value;
         const char *SK = reinterpret_cast<const char *>(sk[st]);
         const char *SV = reinterpret_cast<const char *>(sv[st]);
+        // the lane's base offsets, re-derived per tile (opaque, as in the dK/dV kernel)
+        uint32_t ka0 = ka0_, va0 = va0_, ta0[2] = {ta0_[0], ta0_[1]};
+        asm volatile("" : "+v"(ka0), "+v"(va0), "+v"(ta0[0]), "+v"(ta0[1]));
         const bool edge = (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
         // the last key this lane's row sees, relative to the lane's first key of the tile
         const int lim = (CAUSAL ? min(qrow + off, p.Nkv - 1) : p.Nkv - 1) - kv0 - 8 * h;
@@ -451,6 +481,13 @@ void bwd_dq_kernel(BwdParams p)
                 s = mfma32(as<V8>(xk), qf[ks], s);
                 dp = mfma32(as<V8>(xv), gf[ks], dp);
             }
+            // hidden pairs: s = -inf before the exponential, in a pass that
+            // only tiles crossing the diagonal or the ragged end take
+            if (edge) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (32 * kk + 16 * (e / 8) + e % 8 > lim) s[e] = -INFINITY;
+            }
             u32x4 dw[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u)
@@ -460,8 +497,7 @@ void bwd_dq_kernel(BwdParams p)
 #pragma unroll
                     for (int b = 0; b < 2; ++b) {
                         const int e = 8 * u + 2 * j + b;
-                        float pe = fast_exp2(fmaf(s[e], cs, -l2));
-                        if (edge && 32 * kk + 16 * u + 2 * j + b > lim) pe = 0.f;
+                        const float pe = fast_exp2(fmaf(s[e], cs, -l2));
                         dr[b] = pe * (dp[e] - dd);
                     }
                     dw[u][j] = pack2<T>(dr[0], dr[1]);
@@ -479,16 +515,22 @@ void bwd_dq_kernel(BwdParams p)
         }
     };
 
-    if (nkb > 0) issue(0, 0);
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int st = kb & 1;
+    // key tile kb sits in stage kb & 1; two tiles per pass, so that the stage
+    // is a constant of each copy
+    auto step = [&](auto stc, int kb) {
+        constexpr int st = decltype(stc)::value;
         wait_vmcnt<0>();
         __syncthreads();
         if (kb + 1 < nkb) issue(st ^ 1, kb + 1);
         const int kv0 = kb * BN;
         // wave-uniform: the products mix operands across lanes, so a wave runs
         // them whole; columns of rows past Nq are formed and never stored
-        if (wq0 < p.Nq && (!CAUSAL || kv0 <= wq0 + 31 + off)) tile(st, kv0);
+        if (wq0 < p.Nq && (!CAUSAL || kv0 <= wq0 + 31 + off)) tile(stc, kv0);
+    };
+    if (nkb > 0) issue(0, 0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        step(std::integral_constant<int, 0>{}, kb);
+        if (kb + 1 < nkb) step(std::integral_constant<int, 1>{}, kb + 1);
     }
 
     if (live) {
