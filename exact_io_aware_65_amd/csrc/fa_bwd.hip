@@ -251,11 +251,22 @@ void bwd_dkdv_kernel(BwdParams p)
         const int qs0 = t * BQ + 32 * qq;  // first query of the sub-tile
         // S = Q K^T and dP = dO V^T (rows: queries in swap23 order; columns: keys)
         f32x16 s = {}, dp = {};
-        // Causal: hidden pairs start the S accumulation at -inf, so that the
-        // product leaves s = -inf and p = 2^(c s - l2) = 0.  Only sub-tiles
-        // that cross the diagonal or the ragged end take this; the common path
-        // has no per-score test.  Element e is query qs0 + 8 h + r(e), r(e) =
-        // 16 (e / 8) + e % 8, visible iff lo <= r(e) < hi.
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint32_t a = (ra0 ^ (ks << 5)) + qq * 32 * ROWB;
+            s = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SQ + a)), kf[ks], s);
+            V8 vb;
+            if constexpr (VLDS)
+                vb = as<V8>(*reinterpret_cast<const u32x4 *>(SV + (va0 ^ (ks << 5))));
+            else
+                vb = vf[ks];
+            dp = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SDO + a)), vb, dp);
+        }
+        // Causal: hidden pairs get s = -inf, so that p = 2^(c s - l2) = 0: a
+        // pass over the scores that only sub-tiles crossing the diagonal or the
+        // ragged end take; the common path has no per-score test.  Element e
+        // is query qs0 + 8 h + r(e), r(e) = 16 (e / 8) + e % 8, visible iff
+        // lo <= r(e) < hi.
         // Without the causal mask the only hidden rows are those past Nq, and
         // they need no test: their Q, dO, l2 and D are read as zeros, so p = 1
         // there but dO = 0 and dS = p (dP - D) = 0, and they add nothing to
@@ -270,17 +281,6 @@ void bwd_dkdv_kernel(BwdParams p)
                     if (static_cast<unsigned>(16 * (e / 8) + e % 8 - lo) >= static_cast<unsigned>(hi - lo))
                         s[e] = -INFINITY;
             }
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const uint32_t a = (ra0 ^ (ks << 5)) + qq * 32 * ROWB;
-            s = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SQ + a)), kf[ks], s);
-            V8 vb;
-            if constexpr (VLDS)
-                vb = as<V8>(*reinterpret_cast<const u32x4 *>(SV + (va0 ^ (ks << 5))));
-            else
-                vb = vf[ks];
-            dp = mfma32(as<V8>(*reinterpret_cast<const u32x4 *>(SDO + a)), vb, dp);
         }
         // this lane's queries: element e <-> query 8 h + e (e < 8), 16 + 8 h + e - 8
         const f32x4 *l2v = reinterpret_cast<const f32x4 *>(&sl2[st][32 * qq + 8 * h]);
