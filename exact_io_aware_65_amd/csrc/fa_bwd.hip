@@ -173,7 +173,7 @@ void bwd_dkdv_kernel(BwdParams p)
     // permuted by kswz of its row; the lane then reads row 32 wave + c, logical
     // chunk 2 s + h, conflict-free as the forward's K reads.
     V8 kf[KS], vf[VLDS ? 1 : KS];
-    uint32_t va0_ = 0;
+    uint32_t va0 = 0;
     {
         const auto rk = make_rsrc(static_cast<const char *>(p.k) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
         const auto rv = make_rsrc(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
@@ -189,7 +189,7 @@ void bwd_dkdv_kernel(BwdParams p)
                 sv[row * DC + (col ^ kswz<D>(row))] = buffer_load16(rv, static_cast<uint32_t>(k0 + row) * ROWB + col * 16, 0);
             }
             const int vrow = 32 * wave + c;
-            va0_ = vrow * ROWB + ((h ^ kswz<D>(vrow)) << 4);
+            va0 = vrow * ROWB + ((h ^ kswz<D>(vrow)) << 4);
         }
     }
     const char *SV = reinterpret_cast<const char *>(sv);
@@ -214,22 +214,22 @@ void bwd_dkdv_kernel(BwdParams p)
 
     // Row reads of Q and dO (A operands of S and dP): row swap23(c) (+ 32 per
     // sub-tile), logical chunk 2 s + h.
-    uint32_t ra0_;
+    uint32_t ra0;
     {
         const int r = swap23(c);
-        ra0_ = r * ROWB + ((h ^ dswz<D>(r)) << 4);
+        ra0 = r * ROWB + ((h ^ dswz<D>(r)) << 4);
     }
     // Transposed reads (A operands of dV^T = dO^T P and dK^T = Q^T dS): lane
     // 16 g + 4 j + q addresses query 8 (g / 2) + j + 4 half (+ 16 u + 32 per
     // sub-tile) and dims 32 dt + 16 (g % 2) + 4 q .. + 3.  The permutation
     // depends on half; dt enters as an XOR on bits 6.. of the offset.
-    uint32_t ta0_[2];
+    uint32_t ta0[2];
     {
         const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int r = 8 * (g >> 1) + j + 4 * half;
-            ta0_[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
+            ta0[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
         }
     }
 
@@ -244,10 +244,6 @@ void bwd_dkdv_kernel(BwdParams p)
         constexpr int st = decltype(stc)::value;
         const char *SQ = reinterpret_cast<const char *>(sq[st]);
         const char *SDO = reinterpret_cast<const char *>(sdo[st]);
-        // the lane's base offsets, re-derived per sub-tile (kept opaque so that
-        // the per-k-step variants are formed here rather than held across the loop)
-        uint32_t ra0 = ra0_, ta0[2] = {ta0_[0], ta0_[1]}, va0 = va0_;
-        asm volatile("" : "+v"(ra0), "+v"(ta0[0]), "+v"(ta0[1]), "+v"(va0));
         const int qs0 = t * BQ + 32 * qq;  // first query of the sub-tile
         // S = Q K^T and dP = dO V^T (rows: queries in swap23 order; columns: keys)
         f32x16 s = {}, dp = {};
@@ -432,20 +428,20 @@ void bwd_dq_kernel(BwdParams p)
     };
 
     // Row reads of K (dswz) and V (kswz): row 32 kk + swap23(c), chunk 2 s + h.
-    uint32_t ka0_, va0_;
+    uint32_t ka0, va0;
     {
         const int r = swap23(c);
-        ka0_ = r * ROWB + ((h ^ dswz<D>(r)) << 4);
-        va0_ = r * ROWB + ((h ^ kswz<D>(r)) << 4);
+        ka0 = r * ROWB + ((h ^ dswz<D>(r)) << 4);
+        va0 = r * ROWB + ((h ^ kswz<D>(r)) << 4);
     }
     // Transposed reads of K (A operand of dQ^T = K^T dS^T), as in the dK/dV kernel.
-    uint32_t ta0_[2];
+    uint32_t ta0[2];
     {
         const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int r = 8 * (g >> 1) + j + 4 * half;
-            ta0_[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
+            ta0[half] = r * ROWB + (((2 * (g & 1) + (q >> 1)) ^ dswz<D>(r)) << 4) + ((q & 1) << 3);
         }
     }
 
@@ -462,9 +458,6 @@ void bwd_dq_kernel(BwdParams p)
         constexpr int st = decltype(stc)::value;
         const char *SK = reinterpret_cast<const char *>(sk[st]);
         const char *SV = reinterpret_cast<const char *>(sv[st]);
-        // the lane's base offsets, re-derived per tile (opaque, as in the dK/dV kernel)
-        uint32_t ka0 = ka0_, va0 = va0_, ta0[2] = {ta0_[0], ta0_[1]};
-        asm volatile("" : "+v"(ka0), "+v"(va0), "+v"(ta0[0]), "+v"(ta0[1]));
         const bool edge = (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
         // the last key this lane's row sees, relative to the lane's first key of the tile
         const int lim = (CAUSAL ? min(qrow + off, p.Nkv - 1) : p.Nkv - 1) - kv0 - 8 * h;
