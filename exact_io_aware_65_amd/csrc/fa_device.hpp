@@ -68,6 +68,15 @@ __device__ __forceinline__ f32x16 mfma32_e4m3(i32x8 a, i32x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// D(16x16, fp32) += A(16x128) * B(128x16) on OCP E4M3 operands.  Lane
+// l = 16 g + i supplies row (A) or column (B) i and the 32 k-slots of group g,
+// byte j of its 8 words being k-slot j of the group, the same way for A and
+// B; D as for mfma16.
+__device__ __forceinline__ f32x4 mfma16_e4m3(i32x8 a, i32x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // fp32 -> E4M3 (OCP): nearest, ties to even; magnitudes beyond the largest
 // finite value 448 (infinities included) saturate; NaN stays NaN.  Four
 // values into one word, the first in the low byte.

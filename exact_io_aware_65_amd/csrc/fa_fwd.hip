@@ -685,7 +685,7 @@ template <int D> constexpr int v16_xor(int i) { return vswz16<D>(i * (1024 / (2 
 template <int ROWB> constexpr int kswz_fn(int row) { return kswz<ROWB>(row); }
 template <int D> constexpr int vswz16_fn(int row) { return vswz16<D>(row); }
 
-template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS>
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8 = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd16_kernel(FwdParams p)
 {
@@ -698,15 +698,25 @@ void fwd16_kernel(FwdParams p)
     constexpr int KS = D / 32;             // k-steps of the first product
     constexpr int DB = D / 16;             // 16-dim blocks of the output
     constexpr int U = lcm2(NS);
+    // KF8: K arrives as E4M3 bytes (d bytes per row) and Q is rounded to E4M3
+    // as it is loaded; S^T = K Q^T then takes one 16x16x128 E4M3 MFMA per
+    // (key block, query block) at d = 128, the rest is unchanged.
+    static_assert(!KF8 || (D == 128 && NW == 8 && NS == 2), "E4M3 K: d = 128, eight waves");
+    constexpr int KROWB = KF8 ? D : ROWB;  // bytes per K row
+    constexpr int KTILE = BN * KROWB / 16; // chunks per K tile
+    constexpr int LOADS_K = KTILE / NT;    // direct loads per thread per K tile
     static_assert(NS >= 2 && TILE % NT == 0 && LOADS >= 1 && LOADS <= 4, "tile must split evenly over the threads");
-    static_assert(load_xor_holds<ROWB, LOADS, NW, kswz_fn<ROWB>>(k16_xor<ROWB>), "K load i is load 0 re-permuted");
+    static_assert(KTILE % NT == 0 && LOADS_K >= 1, "K tile must split evenly over the threads");
+    static_assert(KF8 || load_xor_holds<ROWB, LOADS, NW, kswz_fn<ROWB>>(k16_xor<ROWB>), "K load i is load 0 re-permuted");
     static_assert(load_xor_holds<ROWB, LOADS, NW, vswz16_fn<D>>(v16_xor<D>), "V load i is load 0 re-permuted");
-    static_assert(NS * TILE * 16 <= 65536, "stage offsets must fit the 16-bit LDS immediate");
+    static_assert(NS * (KTILE + TILE) * 16 <= 65536, "stage offsets must fit the 16-bit LDS immediate");
     using V8 = typename Vec<T>::v8;
 
-    __shared__ u32x4 lds_rings[NS * 2 * TILE];
-    u32x4(*const sk)[TILE] = reinterpret_cast<u32x4(*)[TILE]>(lds_rings);
-    u32x4(*const sv)[TILE] = reinterpret_cast<u32x4(*)[TILE]>(lds_rings + NS * TILE);
+    // K and V rings; the O stage of the epilogue reuses them (hence the size)
+    constexpr int RING = NS * (KTILE + TILE), OSTAGE = NW * 32 * ROWB / 16;
+    __shared__ u32x4 lds_rings[RING > OSTAGE ? RING : OSTAGE];
+    u32x4(*const sk)[KTILE] = reinterpret_cast<u32x4(*)[KTILE]>(lds_rings);
+    u32x4(*const sv)[TILE] = reinterpret_cast<u32x4(*)[TILE]>(lds_rings + NS * KTILE);
     if constexpr (kPoisonLds) {
         poison_lds(lds_rings, sizeof(lds_rings));
         __syncthreads();
@@ -733,20 +743,37 @@ void fwd16_kernel(FwdParams p)
     const size_t q_head = static_cast<size_t>(bh) * p.Nq * ROWB;
     const size_t kv_head = static_cast<size_t>(bh) * p.Nkv * ROWB;
     const auto rq = make_rsrc(static_cast<const char *>(p.q) + q_head, static_cast<uint32_t>(p.Nq) * ROWB);
-    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
+    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + (KF8 ? kv_head / 2 : kv_head),
+                                     static_cast<uint32_t>(p.Nkv) * KROWB);
     const u32x4 rv = make_rsrc_words(static_cast<const char *>(p.v) + kv_head, static_cast<uint32_t>(p.Nkv) * ROWB);
 
     // Q operand, loaded once: lane (g, i) holds query wq0 + 16 qb + i, dims
     // 32 s + 8 g .. + 7.
-    V8 qf[2][KS];
+    // KF8: dims 32 g .. + 31 rounded to E4M3 (qf8), the B operand of the one
+    // 128-deep k-step.
+    V8 qf[2][KF8 ? 1 : KS];
+    i32x8 qf8[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb) {
+        if constexpr (KF8) {
+            i32x8 w;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const u32x4 x = buffer_load16(rq, static_cast<uint32_t>(wq0 + 16 * qb + li) * ROWB + (32 * s + 8 * g) * 2, 0) ^
-                            p.qsign;
-            qf[qb][s] = as<V8>(x);
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 x =
+                    buffer_load16(rq, static_cast<uint32_t>(wq0 + 16 * qb + li) * ROWB + (32 * g + 8 * t) * 2, 0) ^ p.qsign;
+                w[2 * t] = static_cast<int>(e4m3x4(lo_f32<T>(x[0]), hi_f32<T>(x[0]), lo_f32<T>(x[1]), hi_f32<T>(x[1])));
+                w[2 * t + 1] = static_cast<int>(e4m3x4(lo_f32<T>(x[2]), hi_f32<T>(x[2]), lo_f32<T>(x[3]), hi_f32<T>(x[3])));
+            }
+            qf8[qb] = w;
+        } else {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 x =
+                    buffer_load16(rq, static_cast<uint32_t>(wq0 + 16 * qb + li) * ROWB + (32 * s + 8 * g) * 2, 0) ^ p.qsign;
+                qf[qb][s] = as<V8>(x);
+            }
         }
+    }
 
     // Direct loads (as in the 32x32 kernel): the wave's load i fills LDS chunks
     // [(wave LOADS + i) 64, + 64); load i is load 0 moved by 1024 i bytes in
@@ -758,6 +785,10 @@ void fwd16_kernel(FwdParams p)
         const int row = pch / DC, col = pch % DC;
         koff0 = row * ROWB + ((col ^ kswz<ROWB>(row)) << 4);
         voff0 = row * ROWB + ((col ^ vswz16<D>(row)) << 4);
+        if constexpr (KF8) {  // one load per thread: 8 rows of 8 chunks per wave
+            const int kch = wave * 64 + lane, krow = kch / (KROWB / 16), kcol = kch % (KROWB / 16);
+            koff0 = krow * KROWB + ((kcol ^ kswz<KROWB>(krow)) << 4);
+        }
     }
     constexpr int kx1 = k16_xor<ROWB>(1), kx2 = k16_xor<ROWB>(2), kx3 = k16_xor<ROWB>(3);
     constexpr int vx1 = v16_xor<D>(1), vx2 = v16_xor<D>(2), vx3 = v16_xor<D>(3);
@@ -769,8 +800,14 @@ void fwd16_kernel(FwdParams p)
         if constexpr (LOADS > 2) dma_to_lds16<2048>(rsrc, off0 ^ (decltype(x2)::value << 4), tile, dst);
         if constexpr (LOADS > 3) dma_to_lds16<3072>(rsrc, off0 ^ (decltype(x3)::value << 4), tile, dst);
     };
+    auto issue_k8 = [&](const u32x4 *dst_tile, int kb) {
+        dma_to_lds16<0>(rk, koff0, static_cast<uint32_t>(kb) * BN * KROWB, dst_tile + wave * 64);
+    };
     auto issue_k = [&](auto st, int kb) {
-        issue(rk, koff0, IC<kx1>{}, IC<kx2>{}, IC<kx3>{}, sk[decltype(st)::value], kb);
+        if constexpr (KF8)
+            issue_k8(sk[decltype(st)::value], kb);
+        else
+            issue(rk, koff0, IC<kx1>{}, IC<kx2>{}, IC<kx3>{}, sk[decltype(st)::value], kb);
     };
     auto issue_v = [&](auto st, int kb) {
         issue(rv, voff0, IC<vx1>{}, IC<vx2>{}, IC<vx3>{}, sv[decltype(st)::value], kb);
@@ -790,6 +827,9 @@ void fwd16_kernel(FwdParams p)
     // K (kb, s): row 16 kb + i, logical chunk 4 s + g; the permutation depends
     // on i only, and chunk 4 s + g is chunk g XOR 4 s.
     const uint32_t ka0 = li * ROWB + ((g ^ kswz<ROWB>(li)) << 4);
+    // KF8: row 16 kb + i, logical chunks 2 g and 2 g + 1 (the 32 k-slots of
+    // group g); the permutation again depends on i only.
+    const uint32_t ka8 = li * KROWB + (((2 * g) ^ kswz<KROWB>(li)) << 4);
     // V^T (db, s, h): the in-group lane i addresses row 4 g + i / 4 (+ 32 s +
     // 16 h) and bytes 32 db + 8 (i % 4) .. + 7, so that lane i receives dims
     // 16 db + i of the four rows; db enters as an XOR on the chunk index, and
@@ -821,8 +861,23 @@ void fwd16_kernel(FwdParams p)
     auto kop = [&](const char *SK, int s, int kb) {
         return *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ ((4 * s) << 4)) + kb * 16 * ROWB);
     };
+    auto kop8 = [&](const char *SK, int kb) {
+        const u32x4 x0 = *reinterpret_cast<const u32x4 *>(SK + ka8 + kb * 16 * KROWB);
+        const u32x4 x1 = *reinterpret_cast<const u32x4 *>(SK + (ka8 ^ 16) + kb * 16 * KROWB);
+        return i32x8{static_cast<int>(x0[0]), static_cast<int>(x0[1]), static_cast<int>(x0[2]), static_cast<int>(x0[3]),
+                     static_cast<int>(x1[0]), static_cast<int>(x1[1]), static_cast<int>(x1[2]), static_cast<int>(x1[3])};
+    };
     auto scores = [&](auto st, Frag &sn) {
         const char *SK = reinterpret_cast<const char *>(sk[decltype(st)::value]);
+        if constexpr (KF8) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const i32x8 a = kop8(SK, kb);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) sn[kb][qb] = mfma16_e4m3(a, qf8[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -1012,7 +1067,12 @@ void fwd16_kernel(FwdParams p)
         auto loads = [&](int j) __attribute__((always_inline)) {
             const int S = j & 1;
             if (j + 1 < nkb) issue(rv, voff0, IC<vx1>{}, IC<vx2>{}, IC<vx3>{}, sv[S ^ 1], j + 1);
-            if (j + 2 < nkb) issue(rk, koff0, IC<kx1>{}, IC<kx2>{}, IC<kx3>{}, sk[S], j + 2);
+            if (j + 2 < nkb) {
+                if constexpr (KF8)
+                    issue_k8(sk[S], j + 2);
+                else
+                    issue(rk, koff0, IC<kx1>{}, IC<kx2>{}, IC<kx3>{}, sk[S], j + 2);
+            }
         };
         auto end_step = [&](int j) __attribute__((always_inline)) {
             wait_loads<LOADS, kMaxWait>(allowance(j));
@@ -1039,6 +1099,22 @@ void fwd16_kernel(FwdParams p)
                 for (int kb = 0; kb < 4; ++kb) kx[s & 1][kb] = kop(SK, s, kb);
             };
             auto vread = [&](int gi) __attribute__((always_inline)) { vx[gi % (kVAhead + 1)] = vop(SV, gi / DB, gi % DB); };
+            if constexpr (KF8) {
+                // the four K operands, then the first V operands, before the
+                // eight score MFMAs (256 cycles: too short to cover the V reads)
+                i32x8 k8[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) k8[kb] = kop8(SK, kb);
+#pragma unroll
+                for (int gi = 0; gi < kVAhead && gi < NG; ++gi) vread(gi);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        sa[kb][qb] = mfma16_e4m3(k8[kb], qf8[qb], f32x4{0.f, 0.f, 0.f, 0.f});
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
             kread(0);
             if constexpr (KS > 1) kread(1);
             __builtin_amdgcn_sched_barrier(0);
@@ -1057,6 +1133,7 @@ void fwd16_kernel(FwdParams p)
                     for (int gi = 0; gi < kVAhead && gi < NG; ++gi) vread(gi);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+            }
             }
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
@@ -1177,6 +1254,9 @@ void fwd16_kernel(FwdParams p)
 // causal workload, deeper rings (3 or 4 stages) were no faster: a step's
 // loads already land within the step, and the chip is power-bound there.
 constexpr int kCUs = 256;
+#ifndef FA355_FP8_16
+#define FA355_FP8_16 1
+#endif
 
 template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, int NS, bool KF8, int KG = 1>
 hipError_t launch_shape(const FwdArgs &a, hipStream_t stream)
@@ -1216,7 +1296,7 @@ Shape pick_shape(const FwdArgs &a)
     // MFMAs better than one 8-wave workgroup: measured 4% faster at 8K d=128.
     // (A d = 64 E4M3 K tile is also exactly one load per thread of 4 waves.)
     const long long wide_blocks = static_cast<long long>(a.B) * a.H * ((a.Nq + 255) / 256);
-    if (!a.k_e4m3 && wide_blocks >= kCUs) return {8, 1};
+    if ((!a.k_e4m3 || (FA355_FP8_16 && a.d == 128)) && wide_blocks >= kCUs) return {8, 1};
     // Too few 128-row tiles to give every CU one: two key groups per tile
     // halve the serial chain of key tiles (worth it from 4 key tiles on).
     // Causal at d = 64 (16-bit K): 64-row tiles of two 2-wave key groups.
@@ -1232,8 +1312,9 @@ Shape pick_shape(const FwdArgs &a)
     return {4, 1};
 }
 
-// The 16x16x32 kernel for 16-bit K in the one-group shapes.
-template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW>
+// The 16x16x32 kernel for 16-bit K in the one-group shapes, and for E4M3 K
+// in the eight-wave shape at d = 128.
+template <int D, typename T, bool CAUSAL, bool OUT_F32, int NW, bool KF8 = false>
 hipError_t launch16(const FwdArgs &a, hipStream_t stream)
 {
     constexpr int BM = 32 * NW;
@@ -1251,7 +1332,7 @@ hipError_t launch16(const FwdArgs &a, hipStream_t stream)
     p.c = c < kMinC ? kMinC : c;
     p.qsign = a.scale < 0.f ? 0x80008000u : 0u;
     const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_qt));
-    hipLaunchKernelGGL((fwd16_kernel<D, T, CAUSAL, OUT_F32, NW, 2>), grid, dim3(64 * NW), 0, stream, p);
+    hipLaunchKernelGGL((fwd16_kernel<D, T, CAUSAL, OUT_F32, NW, 2, KF8>), grid, dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1261,6 +1342,8 @@ template <int D, typename T, bool CAUSAL, bool OUT_F32, bool KF8>
 hipError_t launch_k(const FwdArgs &a, hipStream_t stream)
 {
     const Shape s = pick_shape(a);
+    if constexpr (KF8 && D == 128)
+        if (s.nw == 8 && s.kg == 1) return launch16<D, T, CAUSAL, OUT_F32, 8, true>(a, stream);
     if constexpr (!KF8)
         if (s.kg == 1) return s.nw == 8 ? launch16<D, T, CAUSAL, OUT_F32, 8>(a, stream)
                                         : launch16<D, T, CAUSAL, OUT_F32, 4>(a, stream);

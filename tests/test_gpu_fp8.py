@@ -60,6 +60,11 @@ CASES = [
     (2, 2, 300, 300, 128, True, "bf16"),
     (1, 1, 513, 600, 64, True, "f16"),
     (3, 4, 256, 1024, 128, False, "f16"),
+    # enough 256-row tiles for the eight-wave 16x16x128 E4M3 kernel at d = 128
+    # (B H ceil(Nq / 256) >= 256): ragged, causal with Nq < Nkv, and no mask
+    (2, 128, 300, 330, 128, True, "f16"),
+    (4, 64, 128, 700, 128, True, "f16"),
+    (1, 256, 257, 200, 128, False, "bf16"),
 ]
 
 
