@@ -42,6 +42,9 @@
 namespace fa355 {
 namespace {
 
+#ifndef FA355_DQ16
+#define FA355_DQ16 1
+#endif
 constexpr long long kPrepMaxBlocks = 65536;  // prep grid cap (grid-stride beyond)
 constexpr float kBwdMinC = 1e-30f;  // as the forward: a zero scale keeps -inf * c = -inf
 
@@ -544,6 +547,226 @@ void bwd_dq_kernel(BwdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// dQ on the 16x16x32 MFMA (d = 128): the forward's fragment layout.  Per wave
+// 32 queries as two 16-query blocks qb; per 64-key tile
+//
+//   S^T  (16 keys x 16 queries) = K (16 keys x 32 dims) Q^T     (A: K rows)
+//   dP^T (16 keys x 16 queries) = V (16 keys x 32 dims) dO^T    (A: V rows)
+//   dQ^T (16 dims x 16 queries) += K^T (16 dims x 32 keys) dS^T (A: K read transposed)
+//
+// Lane l = 16 g + i receives, per 16-key block kb, query i and keys 4 g .. + 3;
+// a k-step of the third product takes key blocks 2 s and 2 s + 1, whose keys
+// 4 g .. + 3 are the lane's k-slots, so dS goes to its B operand without
+// moving between lanes (the forward's P).  The K tile is read both as rows
+// and transposed; its chunk permutation dswz16 is conflict-free for both
+// patterns: 16 consecutive rows read one 16-byte chunk each (the permutation
+// is a bijection on row mod 16), and 8 consecutive rows read one 32-byte run
+// each (its chunk pair, permutation / 2 = row mod 8, a bijection on 8 rows).
+__device__ __forceinline__ constexpr int dswz16(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ constexpr int kswz16(int row) { return row & 15; }
+
+template <typename T, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq16_kernel(BwdParams p)
+{
+    constexpr int D = 128, NW = 4, BM = 32 * NW, BN = 64, NT = 64 * NW;
+    constexpr int DC = D / 8, TILE = BN * DC, LOADS = TILE / NT, ROWB = 2 * D, KS = D / 32, DB = D / 16;
+    static_assert(TILE % NT == 0, "tile must split evenly over the threads");
+    using V8 = typename Vec<T>::v8;
+
+    __shared__ u32x4 sk[2][TILE];  // K tiles, dswz16 (row and transposed reads)
+    __shared__ u32x4 sv[2][TILE];  // V tiles, kswz16 (row reads)
+    if constexpr (kPoisonLds) {
+        poison_lds(sk, sizeof(sk));
+        poison_lds(sv, sizeof(sv));
+        __syncthreads();
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, li = lane & 15;
+
+    const int bh = blockIdx.x % p.n_bh;
+    const int qt = p.n_tiles - 1 - static_cast<int>(blockIdx.x / p.n_bh);  // heavy causal tiles first
+    const int q0 = qt * BM;
+    const int wq0 = q0 + 32 * wave;
+    const int off = p.Nkv - p.Nq;
+    int kend = p.Nkv;
+    if constexpr (CAUSAL) kend = min(p.Nkv, min(q0 + BM, p.Nq) + off);
+    const int nkb = (kend + BN - 1) / BN;
+
+    const size_t qh = static_cast<size_t>(bh) * p.Nq * ROWB, kh = static_cast<size_t>(bh) * p.Nkv * ROWB;
+    const u32x4 rk = make_rsrc_words(static_cast<const char *>(p.k) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+    const u32x4 rv = make_rsrc_words(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+
+    // Q (sign of the scale folded in) and dO as B operands: lane (g, i) holds
+    // query wq0 + 16 qb + i, dims 32 s + 8 g .. + 7.
+    V8 qf[2][KS], gf[2][KS];
+    float l2[2], dd[2];
+    {
+        const auto rq = make_rsrc(static_cast<const char *>(p.q) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+        const auto rdo = make_rsrc(static_cast<const char *>(p.dout) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qrow = wq0 + 16 * qb + li;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint32_t o = static_cast<uint32_t>(qrow) * ROWB + (32 * s + 8 * g) * 2;
+                qf[qb][s] = as<V8>(buffer_load16(rq, o, 0) ^ p.sign);
+                gf[qb][s] = as<V8>(buffer_load16(rdo, o, 0));
+            }
+            const bool live = qrow < p.Nq;
+            l2[qb] = live ? p.l2[static_cast<size_t>(bh) * p.Nq + qrow] : 0.f;
+            dd[qb] = live ? p.dd[static_cast<size_t>(bh) * p.Nq + qrow] : 0.f;
+        }
+    }
+
+    // Direct loads: load i of the wave fills LDS chunks [(wave LOADS + i) 64, + 64).
+    auto issue = [&](int st, int kb) {
+        const uint32_t tk = static_cast<uint32_t>(kb) * BN * ROWB;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int pch = (wave * LOADS + i) * 64 + lane;
+            const int row = pch / DC, col = pch % DC;
+            dma_to_lds16(rk, static_cast<uint32_t>(row * ROWB + ((col ^ dswz16(row)) << 4)), tk,
+                         &sk[st][(wave * LOADS + i) * 64]);
+            dma_to_lds16(rv, static_cast<uint32_t>(row * ROWB + ((col ^ kswz16(row)) << 4)), tk,
+                         &sv[st][(wave * LOADS + i) * 64]);
+        }
+    };
+
+    // Row reads (A of S^T and dP^T): row 16 kb + i, logical chunk 4 s + g; the
+    // permutation depends on i only.
+    const uint32_t ka0 = li * ROWB + ((g ^ dswz16(li)) << 4);
+    const uint32_t va0 = li * ROWB + ((g ^ kswz16(li)) << 4);
+    // Transposed reads of K (A of dQ^T): the in-group lane i addresses row
+    // 4 g + i / 4 (+ 32 s + 16 h) and bytes 32 db + 8 (i % 4) .. + 7, receiving
+    // dims 16 db + i of the four rows; db enters as an XOR on the chunk index.
+    uint32_t ta0;
+    {
+        const int row = 4 * g + (li >> 2);
+        ta0 = row * ROWB + ((((li & 3) >> 1) ^ dswz16(row)) << 4) + ((li & 1) << 3);
+    }
+
+    f32x4 dqacc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dqacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float cs = p.c;
+
+    // One 64-key tile as two 32-key halves (key blocks 2 h and 2 h + 1), each
+    // taken through S^T, dP^T, dS and its dQ products before the next: half
+    // the score registers live at once.
+    auto tile = [&](auto stc, int kv0) {
+        constexpr int st = decltype(stc)::value;
+        const char *SK = reinterpret_cast<const char *>(sk[st]);
+        const char *SV = reinterpret_cast<const char *>(sv[st]);
+        const bool edge = (kv0 + BN > p.Nkv) || (CAUSAL && kv0 + BN - 1 > wq0 + off);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // keep the next half's operand reads out of this half (registers)
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 sa[2][2], pa[2][2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) sa[b][qb] = pa[b][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int kb = 2 * h + b;
+                    const u32x4 xk = *reinterpret_cast<const u32x4 *>(SK + (ka0 ^ ((4 * s) << 4)) + kb * 16 * ROWB);
+                    const u32x4 xv = *reinterpret_cast<const u32x4 *>(SV + (va0 ^ ((4 * s) << 4)) + kb * 16 * ROWB);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        sa[b][qb] = mfma16(as<V8>(xk), qf[qb][s], sa[b][qb]);
+                        pa[b][qb] = mfma16(as<V8>(xv), gf[qb][s], pa[b][qb]);
+                    }
+                }
+            // hidden pairs (past Nkv, or above the diagonal) get s = -inf, on
+            // tiles that cross the diagonal or the ragged end only: element
+            // (b, r) is key kv0 + 16 (2 h + b) + 4 g + r
+            if (edge) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    int lim = p.Nkv - 1;
+                    if constexpr (CAUSAL) lim = min(lim, wq0 + 16 * qb + li + off);
+                    const int t = lim - kv0 - 4 * g;
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (16 * (2 * h + b) + r > t) sa[b][qb][r] = -INFINITY;
+                }
+            }
+            // dS = P (dP - D) in the storage type, the B operand of k-step h
+            V8 dsf[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                u32x4 w;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    float e[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        e[r] = fast_exp2(fmaf(sa[b][qb][r], cs, -l2[qb])) * (pa[b][qb][r] - dd[qb]);
+                    w[2 * b] = pack2<T>(e[0], e[1]);
+                    w[2 * b + 1] = pack2<T>(e[2], e[3]);
+                }
+                dsf[qb] = as<V8>(w);
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const char *pa0 = SK + (ta0 ^ (db << 5)) + 32 * h * ROWB;
+                const u32x2 lo = lds_read_tr16(pa0), hi = lds_read_tr16(pa0 + 16 * ROWB);
+                const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) dqacc[db][qb] = mfma16(as<V8>(a), dsf[qb], dqacc[db][qb]);
+            }
+        }
+    };
+
+    // key tile kb sits in stage kb & 1; two tiles per pass, so that the stage
+    // is a constant of each copy
+    auto step = [&](auto stc, int kb) {
+        constexpr int st = decltype(stc)::value;
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (kb + 1 < nkb) issue(st ^ 1, kb + 1);
+        const int kv0 = kb * BN;
+        // wave-uniform: columns of rows past Nq are formed and never stored
+        if (wq0 < p.Nq && (!CAUSAL || kv0 <= wq0 + 31 + off)) tile(stc, kv0);
+    };
+    if (nkb > 0) issue(0, 0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        step(std::integral_constant<int, 0>{}, kb);
+        if (kb + 1 < nkb) step(std::integral_constant<int, 1>{}, kb + 1);
+    }
+
+    // Epilogue: lane (g, i) holds dims 16 db + 4 g .. + 3 of query wq0 + 16 qb + i.
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qrow = wq0 + 16 * qb + li;
+        if (qrow < p.Nq) {
+            const size_t orow = (static_cast<size_t>(bh) * p.Nq + qrow) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d0 = 16 * db + 4 * g;
+                const f32x4 v4 = dqacc[db][qb] * p.scale;
+                if constexpr (OUT_F32)
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dq) + orow + d0) = v4;
+                else
+                    *reinterpret_cast<u32x2 *>(static_cast<T *>(p.dq) + orow + d0) =
+                        u32x2{pack2<T>(v4[0], v4[1]), pack2<T>(v4[2], v4[3])};
+            }
+        }
+    }
+}
+
 template <int D, typename T, bool CAUSAL, bool OUT_F32>
 hipError_t launch(const BwdArgs &a, hipStream_t stream)
 {
@@ -583,8 +806,12 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
 
     p.n_tiles = (a.Nq + 127) / 128;
     if (p.n_tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, OUT_F32>),
-                       dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    if constexpr (D == 128 && FA355_DQ16)
+        hipLaunchKernelGGL((bwd_dq16_kernel<T, CAUSAL, OUT_F32>),
+                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, OUT_F32>),
+                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
