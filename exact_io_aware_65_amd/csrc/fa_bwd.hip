@@ -42,6 +42,9 @@
 namespace fa355 {
 namespace {
 
+#ifndef FA355_DKDV16
+#define FA355_DKDV16 1
+#endif
 #ifndef FA355_DQ16
 #define FA355_DQ16 1
 #endif
@@ -767,6 +770,260 @@ void bwd_dq16_kernel(BwdParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV on the 16x16x32 MFMA (d = 128).  Per wave 32 keys as two 16-key
+// blocks kb; per 32-query sub-tile (two 16-query blocks qb)
+//
+//   S   (16 queries x 16 keys) = Q (16 queries x 32 dims) K^T    (A: Q rows)
+//   dP  (16 queries x 16 keys) = dO (16 queries x 32 dims) V^T   (A: dO rows)
+//   dV^T (16 dims x 16 keys) += dO^T (16 dims x 32 queries) P    (A: dO read transposed)
+//   dK^T (16 dims x 16 keys) += Q^T (16 dims x 32 queries) dS    (A: Q read transposed)
+//
+// Lane l = 16 g + i receives, per query block qb, key i and queries 4 g .. + 3;
+// the 32 queries of a sub-tile are one k-step of the last two products, whose
+// k-slots for the lane are those queries of qb = 0 and 1, so P and dS go to
+// their B operands without moving between lanes.  K^T (the B operand of S)
+// stays in registers; the block's V sits in LDS (read as rows), Q and dO
+// stream through a two-stage ring and are read both as rows and transposed
+// (dswz16).
+template <typename T, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv16_kernel(BwdParams p)
+{
+    constexpr int D = 128, NW = 4, BK = 32 * NW, BQ = 32, NT = 64 * NW;
+    constexpr int DC = D / 8, TILE = BQ * DC, LOADS = TILE / NT, ROWB = 2 * D, KS = D / 32, DB = D / 16;
+    static_assert(TILE % NT == 0 && (BK * DC) % NT == 0, "tiles must split evenly over the threads");
+    using V8 = typename Vec<T>::v8;
+
+    // base-2 LSE and D of the tile's queries: wave 0 fills each stage with one
+    // 64-lane dword load (the second half is the next tile's, unused)
+    __shared__ u32x4 sq[2][TILE];   // Q tiles [query][dim], dswz16
+    __shared__ u32x4 sdo[2][TILE];  // dO tiles [query][dim], dswz16
+    __shared__ float sl2[2][64];
+    __shared__ float sdd[2][64];
+    __shared__ u32x4 sv[BK * DC];   // the block's V [key][dim], kswz16
+    if constexpr (kPoisonLds) {
+        poison_lds(sq, sizeof(sq));
+        poison_lds(sdo, sizeof(sdo));
+        poison_lds(sl2, sizeof(sl2));
+        poison_lds(sdd, sizeof(sdd));
+        poison_lds(sv, sizeof(sv));
+        __syncthreads();
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, li = lane & 15;
+
+    // Causal: key blocks near the start see the most queries; they go first.
+    const int bh = blockIdx.x % p.n_bh;
+    const int kt = static_cast<int>(blockIdx.x / p.n_bh);
+    const int k0 = kt * BK;
+    const int kw0 = k0 + 32 * wave;
+    const int off = p.Nkv - p.Nq;  // row i sees keys j <= i + off
+    const int nqt = (p.Nq + BQ - 1) / BQ;
+    const int t0 = CAUSAL ? max(0, k0 - off) / BQ : 0;
+    const int wfirst = CAUSAL ? kw0 - off : 0;  // the wave's first query row that sees one of its keys
+
+    const size_t qh = static_cast<size_t>(bh) * p.Nq * ROWB, kh = static_cast<size_t>(bh) * p.Nkv * ROWB;
+    const u32x4 rq = make_rsrc_words(static_cast<const char *>(p.q) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+    const u32x4 rdo = make_rsrc_words(static_cast<const char *>(p.dout) + qh, static_cast<uint32_t>(p.Nq) * ROWB);
+    const u32x4 rl2 = make_rsrc_words(p.l2 + static_cast<size_t>(bh) * p.Nq, static_cast<uint32_t>(p.Nq) * 4);
+    const u32x4 rdd = make_rsrc_words(p.dd + static_cast<size_t>(bh) * p.Nq, static_cast<uint32_t>(p.Nq) * 4);
+
+    // K^T as the B operand of S: lane (g, i) holds key kw0 + 16 kb + i, dims
+    // 32 s + 8 g .. + 7 (zeros past Nkv), with the sign of the scale.  The
+    // block's V goes to LDS, each chunk permuted by kswz16 of its row.
+    V8 kf[2][KS];
+    {
+        const auto rk = make_rsrc(static_cast<const char *>(p.k) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+        const auto rv = make_rsrc(static_cast<const char *>(p.v) + kh, static_cast<uint32_t>(p.Nkv) * ROWB);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                kf[kb][s] = as<V8>(buffer_load16(rk, static_cast<uint32_t>(kw0 + 16 * kb + li) * ROWB + (32 * s + 8 * g) * 2, 0) ^
+                                   p.sign);
+#pragma unroll
+        for (int i = 0; i < BK * DC / NT; ++i) {
+            const int ch = i * NT + tid, row = ch / DC, col = ch % DC;
+            sv[row * DC + (col ^ kswz16(row))] = buffer_load16(rv, static_cast<uint32_t>(k0 + row) * ROWB + col * 16, 0);
+        }
+    }
+    const char *SV = reinterpret_cast<const char *>(sv);
+
+    auto issue = [&](int st, int t) {
+        const uint32_t tq = static_cast<uint32_t>(t) * BQ * ROWB;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int pch = (wave * LOADS + i) * 64 + lane;
+            const int row = pch / DC, col = pch % DC;
+            const uint32_t o = static_cast<uint32_t>(row * ROWB + ((col ^ dswz16(row)) << 4));
+            dma_to_lds16(rq, o, tq, &sq[st][(wave * LOADS + i) * 64]);
+            dma_to_lds16(rdo, o, tq, &sdo[st][(wave * LOADS + i) * 64]);
+        }
+        if (wave == 0) {
+            dma_to_lds4(rl2, lane * 4, static_cast<uint32_t>(t) * BQ * 4, &sl2[st][0]);
+            dma_to_lds4(rdd, lane * 4, static_cast<uint32_t>(t) * BQ * 4, &sdd[st][0]);
+        }
+    };
+
+    // Row reads of Q and dO (A of S and dP): row 16 qb + i, logical chunk 4 s + g.
+    const uint32_t ra0 = li * ROWB + ((g ^ dswz16(li)) << 4);
+    // Row reads of V (B of dP): row 32 wave + 16 kb + i, logical chunk 4 s + g.
+    const uint32_t va0 = (32 * wave + li) * ROWB + ((g ^ kswz16(li)) << 4);
+    // Transposed reads of dO and Q (A of dV^T and dK^T): the in-group lane i
+    // addresses row 4 g + i / 4 (+ 16 for the second half of the k-step) and
+    // bytes 32 db + 8 (i % 4) .. + 7, receiving dims 16 db + i of the four rows.
+    uint32_t ta0;
+    {
+        const int row = 4 * g + (li >> 2);
+        ta0 = row * ROWB + ((((li & 3) >> 1) ^ dswz16(row)) << 4) + ((li & 1) << 3);
+    }
+
+    f32x4 dvacc[DB][2], dkacc[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dvacc[db][kb] = dkacc[db][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float cs = p.c;
+
+    auto subtile = [&](auto stc, int t) {
+        constexpr int st = decltype(stc)::value;
+        const char *SQ = reinterpret_cast<const char *>(sq[st]);
+        const char *SDO = reinterpret_cast<const char *>(sdo[st]);
+        const int qs0 = t * BQ;
+        // S and dP: [qb][kb]
+        f32x4 sa[2][2], pa[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sa[qb][kb] = pa[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            V8 vb[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                vb[kb] = as<V8>(*reinterpret_cast<const u32x4 *>(SV + (va0 ^ ((4 * s) << 4)) + kb * 16 * ROWB));
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const uint32_t a = (ra0 ^ ((4 * s) << 4)) + qb * 16 * ROWB;
+                const V8 xq = as<V8>(*reinterpret_cast<const u32x4 *>(SQ + a));
+                const V8 xd = as<V8>(*reinterpret_cast<const u32x4 *>(SDO + a));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    sa[qb][kb] = mfma16(xq, kf[kb][s], sa[qb][kb]);
+                    pa[qb][kb] = mfma16(xd, vb[kb], pa[qb][kb]);
+                }
+            }
+        }
+        // Causal: hidden pairs get s = -inf, on sub-tiles that cross the
+        // diagonal or the ragged end only; element (qb, kb, r) is query
+        // qs0 + 16 qb + 4 g + r and key kw0 + 16 kb + i.  Without the causal
+        // mask the only hidden rows are those past Nq, and they need no test:
+        // their Q, dO, l2 and D are read as zeros, so p = 1 there but dO = 0
+        // and dS = p (dP - D) = 0, and they add nothing to dV or dK.
+        if constexpr (CAUSAL) {
+            if (qs0 + BQ > p.Nq || kw0 + 31 > qs0 + off) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    // query q sees the key iff q >= key - off, and q < Nq
+                    const int lo = kw0 + 16 * kb + li - off - qs0 - 4 * g, hi = p.Nq - qs0 - 4 * g;
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int q = 16 * qb + r;
+                            if (q < lo || q >= hi) sa[qb][kb][r] = -INFINITY;
+                        }
+                }
+            }
+        }
+        // P and dS into the B operands of the last two products: operand kb
+        // holds, for key 16 kb + i, queries 4 g .. + 3 of qb = 0 then qb = 1
+        const f32x4 l2a[2] = {*reinterpret_cast<const f32x4 *>(&sl2[st][4 * g]),
+                              *reinterpret_cast<const f32x4 *>(&sl2[st][16 + 4 * g])};
+        const f32x4 dda[2] = {*reinterpret_cast<const f32x4 *>(&sdd[st][4 * g]),
+                              *reinterpret_cast<const f32x4 *>(&sdd[st][16 + 4 * g])};
+        V8 pw[2], dw[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            u32x4 wp, wd;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float pe[4], de[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pe[r] = fast_exp2(fmaf(sa[qb][kb][r], cs, -l2a[qb][r]));
+                    de[r] = pe[r] * (pa[qb][kb][r] - dda[qb][r]);
+                }
+                wp[2 * qb] = pack2<T>(pe[0], pe[1]);
+                wp[2 * qb + 1] = pack2<T>(pe[2], pe[3]);
+                wd[2 * qb] = pack2<T>(de[0], de[1]);
+                wd[2 * qb + 1] = pack2<T>(de[2], de[3]);
+            }
+            pw[kb] = as<V8>(wp);
+            dw[kb] = as<V8>(wd);
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS (their transposed reads stay below
+        // the VALU block)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const uint32_t a = ta0 ^ (db << 5);
+            const u32x2 dlo = lds_read_tr16(SDO + a), dhi = lds_read_tr16(SDO + a + 16 * ROWB);
+            const u32x2 qlo = lds_read_tr16(SQ + a), qhi = lds_read_tr16(SQ + a + 16 * ROWB);
+            const V8 ad = as<V8>(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]});
+            const V8 aq = as<V8>(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                dvacc[db][kb] = mfma16(ad, pw[kb], dvacc[db][kb]);
+                dkacc[db][kb] = mfma16(aq, dw[kb], dkacc[db][kb]);
+            }
+        }
+    };
+
+    // tile t sits in stage (t - t0) & 1; two tiles per pass
+    auto step = [&](auto stc, int t) {
+        constexpr int st = decltype(stc)::value;
+        wait_vmcnt<0>();
+        __syncthreads();  // tile t visible to every wave; tile t - 1's stage free
+        if (t + 1 < nqt) issue(st ^ 1, t + 1);
+        const int qs0 = t * BQ;
+        // some (query, key) pair of the sub-tile is visible to this wave
+        if (qs0 < p.Nq && (!CAUSAL || qs0 + BQ - 1 >= wfirst)) subtile(stc, t);
+    };
+    if (t0 < nqt) issue(0, t0);
+    for (int t = t0; t < nqt; t += 2) {
+        step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+
+    // Epilogue: lane (g, i) holds dims 16 db + 4 g .. + 3 of key kw0 + 16 kb + i.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw0 + 16 * kb + li;
+        if (key < p.Nkv) {
+            const size_t orow = (static_cast<size_t>(bh) * p.Nkv + key) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d0 = 16 * db + 4 * g;
+                const f32x4 v4 = dvacc[db][kb];
+                const f32x4 k4 = dkacc[db][kb] * p.scale;
+                if constexpr (OUT_F32) {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dv) + orow + d0) = v4;
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dk) + orow + d0) = k4;
+                } else {
+                    *reinterpret_cast<u32x2 *>(static_cast<T *>(p.dv) + orow + d0) =
+                        u32x2{pack2<T>(v4[0], v4[1]), pack2<T>(v4[2], v4[3])};
+                    *reinterpret_cast<u32x2 *>(static_cast<T *>(p.dk) + orow + d0) =
+                        u32x2{pack2<T>(k4[0], k4[1]), pack2<T>(k4[2], k4[3])};
+                }
+            }
+        }
+    }
+}
+
 template <int D, typename T, bool CAUSAL, bool OUT_F32>
 hipError_t launch(const BwdArgs &a, hipStream_t stream)
 {
@@ -800,8 +1057,12 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
     p.sign = a.scale < 0.f ? 0x80008000u : 0u;
 
     p.n_tiles = (a.Nkv + 127) / 128;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, OUT_F32>),
-                       dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    if constexpr (D == 128 && FA355_DKDV16)
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, CAUSAL, OUT_F32>),
+                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, OUT_F32>),
+                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     p.n_tiles = (a.Nq + 127) / 128;
