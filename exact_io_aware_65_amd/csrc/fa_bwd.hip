@@ -563,11 +563,41 @@ void bwd_dq_kernel(BwdParams p)
 // 4 g .. + 3 are the lane's k-slots, so dS goes to its B operand without
 // moving between lanes (the forward's P).  The K tile is read both as rows
 // and transposed; its chunk permutation dswz16 is conflict-free for both
-// patterns: 16 consecutive rows read one 16-byte chunk each (the permutation
-// is a bijection on row mod 16), and 8 consecutive rows read one 32-byte run
-// each (its chunk pair, permutation / 2 = row mod 8, a bijection on 8 rows).
-__device__ __forceinline__ constexpr int dswz16(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-__device__ __forceinline__ constexpr int kswz16(int row) { return row & 15; }
+// patterns.  A ds_read_b128 is served in four groups of 16 lanes: in each
+// half-wave, the lane quads whose three index bits have even parity form one
+// group and the odd ones the other (measured: lane 0 shares banks with lanes
+// 1-3, 12-15 and 20-27 only).  For rows i = lane % 16 at chunk g ^ p(i), a
+// group holds rows {0-3, 12-15} of one g and rows {4-11} of the other, so p
+// must separate those two sets from each other under XOR by 1; row & 15 and
+// the p below do, ((row & 7) << 1) | (row >> 3) does not (2-way conflicts).
+// A transposed read covers 8 consecutive rows x 32 bytes per 32 lanes, so
+// p / 2 must be a bijection on rows 0-7 and on rows 8-15: here it is
+// (row & 7) XOR 4 (row >> 3).
+__host__ __device__ __forceinline__ constexpr int dswz16(int row) { return (((row & 7) ^ ((row >> 1) & 4)) << 1) | ((row >> 3) & 1); }
+__host__ __device__ __forceinline__ constexpr int kswz16(int row) { return row & 15; }
+
+// The b128 condition above for a row permutation p, checked lane by lane: two
+// lanes of one group (same half-wave, same quad parity) never read the same
+// chunk of different rows.
+template <int (*P)(int)> constexpr bool b128_conflict_free()
+{
+    for (int a = 0; a < 64; ++a)
+        for (int b = a + 1; b < 64; ++b) {
+            const int qa = (a >> 2) & 7, qb = (b >> 2) & 7;
+            const bool same_group = (a >> 5) == (b >> 5) && (__builtin_popcount(qa) & 1) == (__builtin_popcount(qb) & 1);
+            if (same_group && (a & 15) != (b & 15) && ((a >> 4) ^ P(a & 15)) == ((b >> 4) ^ P(b & 15))) return false;
+        }
+    return true;
+}
+template <int (*P)(int)> constexpr bool tr_conflict_free()
+{
+    for (int a = 0; a < 16; ++a)
+        for (int b = a + 1; b < 16; ++b)
+            if ((a >> 3) == (b >> 3) && (P(a) >> 1) == (P(b) >> 1)) return false;
+    return true;
+}
+static_assert(b128_conflict_free<dswz16>() && tr_conflict_free<dswz16>(), "dswz16: conflict-free row and transposed reads");
+static_assert(b128_conflict_free<kswz16>(), "kswz16: conflict-free row reads");
 
 template <typename T, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
