@@ -73,7 +73,8 @@ struct PrepParams {
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 // Chunk permutations (XOR on the 16-byte chunk index of a row).
-// kswz: rows read as 16-byte runs only (16 lanes, rows swap23(0..15)).
+// kswz: rows read as 16-byte runs only (a b128 group of 16 lanes holds rows
+// swap23 of its lanes, 16 rows with distinct low four bits).
 // dswz: rows read both as 16-byte runs and transposed (32 lanes covering 4
 // consecutive rows x 64 bytes).  d = 128: the row's low nibble with its two
 // halves exchanged; d = 64: bit 1 of the row to chunk bit 2, bits 2-3 to

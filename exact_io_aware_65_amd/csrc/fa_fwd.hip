@@ -86,18 +86,20 @@ template <int N> using IC = std::integral_constant<int, N>;
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 // XOR permutations of the 16-byte chunk index within a row, as functions of
-// the row.  K is read as 16-byte runs by 16 lanes holding rows swap23(0..15)
-// (+ a multiple of 16) at one logical chunk: the permutation must send those
-// 16 rows to 16 distinct 16-byte bank groups.  V is read transposed: 32 lanes
+// the row.  K is read as 16-byte runs, one logical chunk per half-wave: a
+// b128 group of 16 lanes (lanes {0-3, 12-15, 20-27} and the like, see the
+// file comment) holds rows swap23 of those lanes, i.e. rows {0-3, 12-15,
+// 20-27} mod 32, whose low four bits are all distinct: the permutation must
+// send those 16 rows to 16 distinct 16-byte bank groups.  V is read transposed: 32 lanes
 // cover 4 consecutive rows (starting at a multiple of 4) x 64 bytes, so the 4
 // rows must land in 4 distinct 64-byte bank segments.  For d = 64 two rows
 // share one 256-byte bank line, hence the extra shift by one row bit.
 //
 // K rows are 2d bytes (16-bit K) or d bytes (E4M3 K): 256, 128 or 64 bytes,
 // i.e. one, a half or a quarter of a 256-byte bank line.  The 16 rows read
-// together are 16 consecutive rows, so the row bits below the line take the
-// low bits of the bank-group index and the rest of the XOR spreads the rows
-// that share them.
+// together differ in their low four bits, so the row bits below the line take
+// the low bits of the bank-group index and the rest of the XOR spreads the
+// rows that share them.
 template <int ROWB> __host__ __device__ constexpr int kswz(int row)
 {
     static_assert(ROWB == 256 || ROWB == 128 || ROWB == 64, "K rows of 256, 128 or 64 bytes");
