@@ -32,6 +32,7 @@ host's cores; it is a reference point, not the target.
     python bench.py --sweep [--steps K] [--warmup W]   # fused vs unfused over sequence length
     python bench.py --map [--steps K] [--warmup W]     # fused kernels over N, d, mask, type
     python bench.py --data-probe [--steps K] [--warmup W]  # fa_fwd on workload, zero and constant inputs
+    python bench.py --lds-probe                        # LDS access patterns, one launch each (for rocprofv3)
 """
 from __future__ import annotations
 
@@ -698,6 +699,132 @@ def run_map(warmup, steps):
 DATA_PROBE = ("prefill_8k_d128", "prefill_16k_d128_bf16")
 
 
+LDS_SKIP = 0xFFFFFFFF
+
+
+def _swap23(x):
+    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1)
+
+
+def lds_probe_patterns():
+    """LDS access patterns for the bank probe (libfa355_probe fa_probe_lds):
+    (name, kind, 64 lane byte offsets), kind 0 = ds_read_b128, 1 =
+    ds_read_b64_tr_b16; LDS_SKIP marks a lane that does not read.
+
+    First, pairs: lane 0 at byte 0 and lane b at byte 256 (the same banks, a
+    different address), the other lanes idle; a conflict means the hardware
+    serves lanes 0 and b in the same cycle.  Then the row reads and
+    transposed reads of the kernels' LDS tiles, as the kernels address them
+    (lane l = 16 g + i of the 16x16x32 fragment layout; rows of 256 bytes,
+    128 for E4M3 K), under their chunk permutations and under the first
+    versions they replaced, and two controls."""
+    pats = []
+    for b in range(1, 64):
+        offs = [LDS_SKIP] * 64
+        offs[0], offs[b] = 0, 256
+        pats.append((f"pair: lane 0 and lane {b}", 0, offs))
+
+    def rows16(chunk_of, rowb=256):
+        return [(l & 15) * rowb + (chunk_of(l >> 4, l & 15) << 4) for l in range(64)]
+
+    def dual_old(r):
+        return ((r & 7) << 1) | ((r >> 3) & 1)
+
+    def dual(r):
+        return (((r & 7) ^ ((r >> 1) & 4)) << 1) | ((r >> 3) & 1)
+
+    pats += [
+        ("b128 16-bit K rows (16x16x32 forward): chunk g ^ (row & 15)", 0, rows16(lambda g, i: g ^ (i & 15))),
+        ("b128 dual-read tiles, first version: chunk g ^ ((row & 7) << 1 | row >> 3)", 0,
+         rows16(lambda g, i: g ^ dual_old(i))),
+        ("b128 dual-read tiles (backward Q, dO, K): chunk g ^ (((row & 7) ^ (row >> 1 & 4)) << 1 | row >> 3)", 0,
+         rows16(lambda g, i: g ^ dual(i))),
+        ("b128 E4M3 K rows of 128 bytes, first version: chunk 2g ^ (row >> 1 & 7)", 0,
+         rows16(lambda g, i: (2 * g) ^ ((i >> 1) & 7), 128)),
+        ("b128 E4M3 K rows of 128 bytes (16x16x128 forward): chunk 2g ^ (row & 6 | row >> 3)", 0,
+         rows16(lambda g, i: (2 * g) ^ ((i & 6) | ((i >> 3) & 1)), 128)),
+        ("b128 16-bit K rows (32x32x16 kernels): lane l reads row swap23(l % 32) at chunk l / 32 ^ (row & 15)", 0,
+         [_swap23(l & 31) * 256 + (((l >> 5) ^ (_swap23(l & 31) & 15)) << 4) for l in range(64)]),
+        ("b128 control: rows 0-15 at chunk g (16 rows in one bank group)", 0, rows16(lambda g, i: g)),
+    ]
+
+    def tr(perm):
+        out = []
+        for l in range(64):
+            g, i = l >> 4, l & 15
+            row = 4 * g + (i >> 2)
+            out.append(row * 256 + ((((i & 3) >> 1) ^ perm(row)) << 4) + ((i & 1) << 3))
+        return out
+
+    pats += [
+        ("tr V^T (16x16x32 forward): 8 rows x 32 bytes per half-wave, chunk pair 2 (row & 7)", 1, tr(lambda r: 2 * (r & 7))),
+        ("tr dual-read tiles (backward Q, dO, K)", 1, tr(dual)),
+        ("tr control: 8 rows at one chunk pair", 1, tr(lambda r: 0)),
+    ]
+    return pats
+
+
+def lds_model_conflict_degree(kind, offsets):
+    """Bank-conflict degree of one pattern under the bank model the kernels'
+    permutations are built for: 64 banks of 4 bytes (address bits 2-7); a
+    ds_read_b128 served in four groups of 16 lanes (in each half-wave, the
+    lane quads whose three index bits have even parity, and the odd ones), a
+    ds_read_b64_tr_b16 in two groups of 32 (the half-waves).  Returns the
+    largest number of distinct dwords one bank serves within a group."""
+    size = 16 if kind == 0 else 8
+    groups = {}
+    for l, o in enumerate(offsets):
+        if o == LDS_SKIP:
+            continue
+        key = (l >> 5, bin((l >> 2) & 7).count("1") & 1) if kind == 0 else (l >> 5,)
+        groups.setdefault(key, []).append(o)
+    worst = 1
+    for offs in groups.values():
+        banks = {}
+        for o in offs:
+            for w in range(size // 4):
+                dw = o // 4 + w
+                banks.setdefault(dw % 64, set()).add(dw)
+        worst = max(worst, max(len(v) for v in banks.values()))
+    return worst
+
+
+def run_lds_probe(blocks=256, iters=1024):
+    """One launch per pattern of lds_probe_patterns(), in order (a warm-up
+    launch of the first pattern precedes them).  Prints what each launch read;
+    run under rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS to get each
+    pattern's conflict cycles per instruction."""
+    import ctypes
+
+    import torch
+    from exact_io_aware_65_amd import build as libbuild
+    if not os.path.exists(libbuild.PROBE_LIBRARY):
+        raise RuntimeError(f"{libbuild.PROBE_LIBRARY} is missing: run python -m exact_io_aware_65_amd.build")
+    lib = ctypes.CDLL(libbuild.PROBE_LIBRARY)
+    lib.fa_probe_lds.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_uint), ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_probe_lds.restype = ctypes.c_int
+    sink = torch.empty(blocks * 64, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    pats = lds_probe_patterns()
+    out = []
+    for n, (name, kind, offs) in enumerate([pats[0]] + pats):
+        arr = (ctypes.c_uint * 64)(*offs)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = lib.fa_probe_lds(kind, arr, blocks, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        b.record(stream)
+        if rc:
+            raise RuntimeError(f"fa_probe_lds failed ({rc}) on pattern {name}")
+        torch.cuda.synchronize()
+        if n == 0:
+            continue  # warm-up launch
+        out.append({"pattern": name, "read": "ds_read_b128" if kind == 0 else "ds_read_b64_tr_b16",
+                    "active_lanes": sum(o != LDS_SKIP for o in offs), "ms": round(a.elapsed_time(b), 4),
+                    "model_conflict_degree": lds_model_conflict_degree(kind, offs)})
+    return {"blocks": blocks, "iters": iters, "patterns": out}
+
+
 def run_data_probe(warmup, steps, rounds=6):
     """fa_fwd on the two long prefill workloads with three kinds of input of
     the same shapes: the seeded workload inputs, all zeros, and constants
@@ -977,6 +1104,8 @@ def main():
                     help="only run the speed map of the fused kernels over sequence length, head dim, mask and type")
     ap.add_argument("--data-probe", action="store_true",
                     help="only time fa_fwd on the long prefill workloads (and fa_decode as a control) with workload, all-zero and constant inputs")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="only run the LDS bank probe (one launch per access pattern; counters from rocprofv3)")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the timing of the other prefill workloads (2K d64, 16K d128 bf16)")
     ap.add_argument("--no-fp8", action="store_true",
@@ -998,6 +1127,13 @@ def main():
         res = run_map(max(1, args.warmup), max(1, args.steps))
         print(json.dumps({"metric": "fused kernel speed over shapes", "unit": "TFLOP/s, GB/s",
                           "higher_is_better": True, "data": "synthetic", "map": res}), flush=True)
+        return
+    if args.lds_probe:
+        if args.gpus != 1:
+            sys.exit("bench.py --lds-probe measures one GPU only")
+        res = run_lds_probe()
+        print(json.dumps({"metric": "LDS access patterns, one launch each (bank conflicts from SQ_LDS_BANK_CONFLICT)",
+                          "unit": "ms", "higher_is_better": False, "data": "synthetic", "lds_probe": res}), flush=True)
         return
     if args.data_probe:
         if args.gpus != 1:

@@ -4,8 +4,9 @@
 
 Each source compiles to its own object (in parallel) under _build/, then the
 objects link into exact_io_aware_65_amd/libfa355.so.  The streaming-read probe
-that bench.py reports decode against (probe/read_bw.hip) builds into its own
-library, exact_io_aware_65_amd/libfa355_probe.so.
+that bench.py reports decode against (probe/read_bw.hip) and the LDS bank probe
+(probe/lds_banks.hip, bench.py --lds-probe) build into their own library,
+exact_io_aware_65_amd/libfa355_probe.so.
 
     python -m exact_io_aware_65_amd.build --poison-lds
 
@@ -28,7 +29,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "libfa355.so")
 BUILD_INFO = os.path.join(PKG, "build_info.json")
-PROBE_SOURCE = os.path.join(PKG, "probe", "read_bw.hip")
+PROBE_SOURCES = [os.path.join(PKG, "probe", "read_bw.hip"), os.path.join(PKG, "probe", "lds_banks.hip")]
 PROBE_LIBRARY = os.path.join(PKG, "libfa355_probe.so")
 POISON_LIBRARY = os.path.join(PKG, "libfa355_poison_lds.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -74,9 +75,10 @@ def build_poison_lds(verbose: bool = False) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
-    for lib, parts in ((LIBRARY, objs[:-1]), (PROBE_LIBRARY, objs[-1:])):
+    with ThreadPoolExecutor(len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    n = len(SOURCES)
+    for lib, parts in ((LIBRARY, objs[:n]), (PROBE_LIBRARY, objs[n:])):
         tmp = lib + ".tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *parts, "-o", tmp]
         if verbose:
