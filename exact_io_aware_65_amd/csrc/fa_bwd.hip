@@ -48,7 +48,15 @@ namespace {
 #ifndef FA355_DQ16
 #define FA355_DQ16 1
 #endif
+#ifndef FA355_BWD16_D64
+#define FA355_BWD16_D64 1
+#endif
 constexpr long long kPrepMaxBlocks = 65536;  // prep grid cap (grid-stride beyond)
+// At d = 64 the 16x16x32 passes are faster once the grid gives every CU two
+// workgroups (8K causal fp16: 679 -> 710 TFLOP/s, 16K bf16: 736 -> 763), and
+// slower below that (2K, B H = 16, one workgroup per CU: 258 -> 235), where
+// the 32x32 passes, whose key-block pass covers 64-row query tiles, stay.
+constexpr long long kBwd16MinBlocksD64 = 2 * 256;
 constexpr float kBwdMinC = 1e-30f;  // as the forward: a zero scale keeps -inf * c = -inf
 
 struct BwdParams {
@@ -577,40 +585,67 @@ void bwd_dq_kernel(BwdParams p)
 __host__ __device__ __forceinline__ constexpr int dswz16(int row) { return (((row & 7) ^ ((row >> 1) & 4)) << 1) | ((row >> 3) & 1); }
 __host__ __device__ __forceinline__ constexpr int kswz16(int row) { return row & 15; }
 
+// d = 64: rows of 128 bytes, two to a bank line (row parity picks the half).
+// The same two conditions hold for row & 6 (rows read both ways) and
+// (row >> 1) & 7 (rows read as rows only): in a row read each parity's eight
+// rows of a group take distinct chunks, and in a transposed read the four
+// rows of each parity among 8 consecutive rows take distinct 32-byte runs.
+__host__ __device__ __forceinline__ constexpr int dswz16h(int row) { return row & 6; }
+__host__ __device__ __forceinline__ constexpr int kswz16h(int row) { return (row >> 1) & 7; }
+template <int ROWB> __host__ __device__ __forceinline__ constexpr int dual16(int row)
+{
+    return ROWB == 256 ? dswz16(row) : dswz16h(row);
+}
+template <int ROWB> __host__ __device__ __forceinline__ constexpr int rows16(int row)
+{
+    return ROWB == 256 ? kswz16(row) : kswz16h(row);
+}
+
 // The b128 condition above for a row permutation p, checked lane by lane: two
 // lanes of one group (same half-wave, same quad parity) never read the same
-// chunk of different rows.
-template <int (*P)(int)> constexpr bool b128_conflict_free()
+// 16-byte slot of the bank line at different addresses.  Lane 16 g + i reads
+// row i at logical chunk g.
+template <int (*P)(int), int ROWB> constexpr bool b128_conflict_free()
 {
+    auto slot = [](int lane) {
+        const int row = lane & 15, chunk = (lane >> 4) ^ P(row);
+        return ROWB == 256 ? chunk : (8 * (row & 1) + chunk) & 15;
+    };
     for (int a = 0; a < 64; ++a)
         for (int b = a + 1; b < 64; ++b) {
             const int qa = (a >> 2) & 7, qb = (b >> 2) & 7;
             const bool same_group = (a >> 5) == (b >> 5) && (__builtin_popcount(qa) & 1) == (__builtin_popcount(qb) & 1);
-            if (same_group && (a & 15) != (b & 15) && ((a >> 4) ^ P(a & 15)) == ((b >> 4) ^ P(b & 15))) return false;
+            if (same_group && (a & 15) != (b & 15) && slot(a) == slot(b)) return false;
         }
     return true;
 }
-template <int (*P)(int)> constexpr bool tr_conflict_free()
+// Transposed reads: 8 consecutive rows x 32 bytes per half-wave; each row's
+// 32-byte run (chunk pair P(row) / 2) must land in its own run of the line.
+template <int (*P)(int), int ROWB> constexpr bool tr_conflict_free()
 {
+    auto run = [](int row) { return ROWB == 256 ? (P(row) >> 1) : 4 * (row & 1) + ((P(row) >> 1) & 3); };
     for (int a = 0; a < 16; ++a)
         for (int b = a + 1; b < 16; ++b)
-            if ((a >> 3) == (b >> 3) && (P(a) >> 1) == (P(b) >> 1)) return false;
+            if ((a >> 3) == (b >> 3) && run(a) == run(b)) return false;
     return true;
 }
-static_assert(b128_conflict_free<dswz16>() && tr_conflict_free<dswz16>(), "dswz16: conflict-free row and transposed reads");
-static_assert(b128_conflict_free<kswz16>(), "kswz16: conflict-free row reads");
+static_assert(b128_conflict_free<dswz16, 256>() && tr_conflict_free<dswz16, 256>(), "dswz16: conflict-free row and transposed reads");
+static_assert(b128_conflict_free<kswz16, 256>(), "kswz16: conflict-free row reads");
+static_assert(b128_conflict_free<dswz16h, 128>() && tr_conflict_free<dswz16h, 128>(), "dswz16h: conflict-free row and transposed reads");
+static_assert(b128_conflict_free<kswz16h, 128>(), "kswz16h: conflict-free row reads");
 
-template <typename T, bool CAUSAL, bool OUT_F32>
+template <int D, typename T, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq16_kernel(BwdParams p)
 {
-    constexpr int D = 128, NW = 4, BM = 32 * NW, BN = 64, NT = 64 * NW;
+    static_assert(D == 64 || D == 128, "d = 64 or 128");
+    constexpr int NW = 4, BM = 32 * NW, BN = 64, NT = 64 * NW;
     constexpr int DC = D / 8, TILE = BN * DC, LOADS = TILE / NT, ROWB = 2 * D, KS = D / 32, DB = D / 16;
     static_assert(TILE % NT == 0, "tile must split evenly over the threads");
     using V8 = typename Vec<T>::v8;
 
-    __shared__ u32x4 sk[2][TILE];  // K tiles, dswz16 (row and transposed reads)
-    __shared__ u32x4 sv[2][TILE];  // V tiles, kswz16 (row reads)
+    __shared__ u32x4 sk[2][TILE];  // K tiles, dual16 (row and transposed reads)
+    __shared__ u32x4 sv[2][TILE];  // V tiles, rows16 (row reads)
     if constexpr (kPoisonLds) {
         poison_lds(sk, sizeof(sk));
         poison_lds(sv, sizeof(sv));
@@ -663,24 +698,24 @@ void bwd_dq16_kernel(BwdParams p)
         for (int i = 0; i < LOADS; ++i) {
             const int pch = (wave * LOADS + i) * 64 + lane;
             const int row = pch / DC, col = pch % DC;
-            dma_to_lds16(rk, static_cast<uint32_t>(row * ROWB + ((col ^ dswz16(row)) << 4)), tk,
+            dma_to_lds16(rk, static_cast<uint32_t>(row * ROWB + ((col ^ dual16<ROWB>(row)) << 4)), tk,
                          &sk[st][(wave * LOADS + i) * 64]);
-            dma_to_lds16(rv, static_cast<uint32_t>(row * ROWB + ((col ^ kswz16(row)) << 4)), tk,
+            dma_to_lds16(rv, static_cast<uint32_t>(row * ROWB + ((col ^ rows16<ROWB>(row)) << 4)), tk,
                          &sv[st][(wave * LOADS + i) * 64]);
         }
     };
 
     // Row reads (A of S^T and dP^T): row 16 kb + i, logical chunk 4 s + g; the
     // permutation depends on i only.
-    const uint32_t ka0 = li * ROWB + ((g ^ dswz16(li)) << 4);
-    const uint32_t va0 = li * ROWB + ((g ^ kswz16(li)) << 4);
+    const uint32_t ka0 = li * ROWB + ((g ^ dual16<ROWB>(li)) << 4);
+    const uint32_t va0 = li * ROWB + ((g ^ rows16<ROWB>(li)) << 4);
     // Transposed reads of K (A of dQ^T): the in-group lane i addresses row
     // 4 g + i / 4 (+ 32 s + 16 h) and bytes 32 db + 8 (i % 4) .. + 7, receiving
     // dims 16 db + i of the four rows; db enters as an XOR on the chunk index.
     uint32_t ta0;
     {
         const int row = 4 * g + (li >> 2);
-        ta0 = row * ROWB + ((((li & 3) >> 1) ^ dswz16(row)) << 4) + ((li & 1) << 3);
+        ta0 = row * ROWB + ((((li & 3) >> 1) ^ dual16<ROWB>(row)) << 4) + ((li & 1) << 3);
     }
 
     f32x4 dqacc[DB][2];
@@ -817,22 +852,23 @@ void bwd_dq16_kernel(BwdParams p)
 // stays in registers; the block's V sits in LDS (read as rows), Q and dO
 // stream through a two-stage ring and are read both as rows and transposed
 // (dswz16).
-template <typename T, bool CAUSAL, bool OUT_F32>
+template <int D, typename T, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv16_kernel(BwdParams p)
 {
-    constexpr int D = 128, NW = 4, BK = 32 * NW, BQ = 32, NT = 64 * NW;
+    static_assert(D == 64 || D == 128, "d = 64 or 128");
+    constexpr int NW = 4, BK = 32 * NW, BQ = 32, NT = 64 * NW;
     constexpr int DC = D / 8, TILE = BQ * DC, LOADS = TILE / NT, ROWB = 2 * D, KS = D / 32, DB = D / 16;
     static_assert(TILE % NT == 0 && (BK * DC) % NT == 0, "tiles must split evenly over the threads");
     using V8 = typename Vec<T>::v8;
 
     // base-2 LSE and D of the tile's queries: wave 0 fills each stage with one
     // 64-lane dword load (the second half is the next tile's, unused)
-    __shared__ u32x4 sq[2][TILE];   // Q tiles [query][dim], dswz16
-    __shared__ u32x4 sdo[2][TILE];  // dO tiles [query][dim], dswz16
+    __shared__ u32x4 sq[2][TILE];   // Q tiles [query][dim], dual16
+    __shared__ u32x4 sdo[2][TILE];  // dO tiles [query][dim], dual16
     __shared__ float sl2[2][64];
     __shared__ float sdd[2][64];
-    __shared__ u32x4 sv[BK * DC];   // the block's V [key][dim], kswz16
+    __shared__ u32x4 sv[BK * DC];   // the block's V [key][dim], rows16
     if constexpr (kPoisonLds) {
         poison_lds(sq, sizeof(sq));
         poison_lds(sdo, sizeof(sdo));
@@ -878,7 +914,7 @@ void bwd_dkdv16_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < BK * DC / NT; ++i) {
             const int ch = i * NT + tid, row = ch / DC, col = ch % DC;
-            sv[row * DC + (col ^ kswz16(row))] = buffer_load16(rv, static_cast<uint32_t>(k0 + row) * ROWB + col * 16, 0);
+            sv[row * DC + (col ^ rows16<ROWB>(row))] = buffer_load16(rv, static_cast<uint32_t>(k0 + row) * ROWB + col * 16, 0);
         }
     }
     const char *SV = reinterpret_cast<const char *>(sv);
@@ -889,7 +925,7 @@ void bwd_dkdv16_kernel(BwdParams p)
         for (int i = 0; i < LOADS; ++i) {
             const int pch = (wave * LOADS + i) * 64 + lane;
             const int row = pch / DC, col = pch % DC;
-            const uint32_t o = static_cast<uint32_t>(row * ROWB + ((col ^ dswz16(row)) << 4));
+            const uint32_t o = static_cast<uint32_t>(row * ROWB + ((col ^ dual16<ROWB>(row)) << 4));
             dma_to_lds16(rq, o, tq, &sq[st][(wave * LOADS + i) * 64]);
             dma_to_lds16(rdo, o, tq, &sdo[st][(wave * LOADS + i) * 64]);
         }
@@ -900,16 +936,16 @@ void bwd_dkdv16_kernel(BwdParams p)
     };
 
     // Row reads of Q and dO (A of S and dP): row 16 qb + i, logical chunk 4 s + g.
-    const uint32_t ra0 = li * ROWB + ((g ^ dswz16(li)) << 4);
+    const uint32_t ra0 = li * ROWB + ((g ^ dual16<ROWB>(li)) << 4);
     // Row reads of V (B of dP): row 32 wave + 16 kb + i, logical chunk 4 s + g.
-    const uint32_t va0 = (32 * wave + li) * ROWB + ((g ^ kswz16(li)) << 4);
+    const uint32_t va0 = (32 * wave + li) * ROWB + ((g ^ rows16<ROWB>(li)) << 4);
     // Transposed reads of dO and Q (A of dV^T and dK^T): the in-group lane i
     // addresses row 4 g + i / 4 (+ 16 for the second half of the k-step) and
     // bytes 32 db + 8 (i % 4) .. + 7, receiving dims 16 db + i of the four rows.
     uint32_t ta0;
     {
         const int row = 4 * g + (li >> 2);
-        ta0 = row * ROWB + ((((li & 3) >> 1) ^ dswz16(row)) << 4) + ((li & 1) << 3);
+        ta0 = row * ROWB + ((((li & 3) >> 1) ^ dual16<ROWB>(row)) << 4) + ((li & 1) << 3);
     }
 
     f32x4 dvacc[DB][2], dkacc[DB][2];
@@ -1088,22 +1124,28 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream)
     p.sign = a.scale < 0.f ? 0x80008000u : 0u;
 
     p.n_tiles = (a.Nkv + 127) / 128;
-    if constexpr (D == 128 && FA355_DKDV16)
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<T, CAUSAL, OUT_F32>),
-                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, OUT_F32>),
-                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    const dim3 gk(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles));
+    if constexpr (D == 128 && FA355_DKDV16) {
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<D, T, CAUSAL, OUT_F32>), gk, dim3(256), 0, stream, p);
+    } else {
+        if (FA355_DKDV16 && FA355_BWD16_D64 && static_cast<long long>(gk.x) >= kBwd16MinBlocksD64)
+            hipLaunchKernelGGL((bwd_dkdv16_kernel<D, T, CAUSAL, OUT_F32>), gk, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, CAUSAL, OUT_F32>), gk, dim3(256), 0, stream, p);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     p.n_tiles = (a.Nq + 127) / 128;
     if (p.n_tiles == 0) return hipSuccess;
-    if constexpr (D == 128 && FA355_DQ16)
-        hipLaunchKernelGGL((bwd_dq16_kernel<T, CAUSAL, OUT_F32>),
-                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, OUT_F32>),
-                           dim3(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles)), dim3(256), 0, stream, p);
+    const dim3 gq(static_cast<unsigned>(static_cast<long long>(p.n_bh) * p.n_tiles));
+    if constexpr (D == 128 && FA355_DQ16) {
+        hipLaunchKernelGGL((bwd_dq16_kernel<D, T, CAUSAL, OUT_F32>), gq, dim3(256), 0, stream, p);
+    } else {
+        if (FA355_DQ16 && FA355_BWD16_D64 && static_cast<long long>(gq.x) >= kBwd16MinBlocksD64)
+            hipLaunchKernelGGL((bwd_dq16_kernel<D, T, CAUSAL, OUT_F32>), gq, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<D, T, CAUSAL, OUT_F32>), gq, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
