@@ -53,10 +53,15 @@ namespace {
 #endif
 constexpr long long kPrepMaxBlocks = 65536;  // prep grid cap (grid-stride beyond)
 // At d = 64 the 16x16x32 passes are faster once the grid gives every CU two
-// workgroups (8K causal fp16: 679 -> 710 TFLOP/s, 16K bf16: 736 -> 763), and
-// slower below that (2K, B H = 16, one workgroup per CU: 258 -> 235), where
-// the 32x32 passes, whose key-block pass covers 64-row query tiles, stay.
+// workgroups (8K causal fp16: 679 -> 710 TFLOP/s, 16K bf16: 736 -> 763, at two
+// waves per SIMD), and slower below that (2K, B H = 16, one workgroup per CU:
+// 258 -> 235), where the 32x32 passes, whose key-block pass covers 64-row
+// query tiles, stay.
 constexpr long long kBwd16MinBlocksD64 = 2 * 256;
+// Waves per SIMD of the 16x16x32 passes: at d = 64 they fit 168 registers, so
+// three workgroups share a CU (8K fp16: 721 -> 772 TFLOP/s, 4K: 645 -> 717,
+// against two); at d = 128 they need 218-250.
+template <int D> constexpr int kBwd16Waves = D == 64 ? 3 : 2;
 constexpr float kBwdMinC = 1e-30f;  // as the forward: a zero scale keeps -inf * c = -inf
 
 struct BwdParams {
@@ -635,7 +640,7 @@ static_assert(b128_conflict_free<dswz16h, 128>() && tr_conflict_free<dswz16h, 12
 static_assert(b128_conflict_free<kswz16h, 128>(), "kswz16h: conflict-free row reads");
 
 template <int D, typename T, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwd16Waves<D>, kBwd16Waves<D>)))
 void bwd_dq16_kernel(BwdParams p)
 {
     static_assert(D == 64 || D == 128, "d = 64 or 128");
@@ -853,7 +858,7 @@ void bwd_dq16_kernel(BwdParams p)
 // stream through a two-stage ring and are read both as rows and transposed
 // (dswz16).
 template <int D, typename T, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kBwd16Waves<D>, kBwd16Waves<D>)))
 void bwd_dkdv16_kernel(BwdParams p)
 {
     static_assert(D == 64 || D == 128, "d = 64 or 128");
