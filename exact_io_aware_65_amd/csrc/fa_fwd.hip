@@ -1324,6 +1324,11 @@ Shape pick_shape(const FwdArgs &a)
     // MFMAs better than one 8-wave workgroup: measured 4% faster at 8K d=128.
     // (A d = 64 E4M3 K tile is also exactly one load per thread of 4 waves.)
     const long long wide_blocks = static_cast<long long>(a.B) * a.H * ((a.Nq + 255) / 256);
+    // Causal at d = 64 with one 256-row tile per CU: each CU's time is its
+    // tile's, so the heaviest sets the kernel's; 128-row tiles two to a CU
+    // balance better (4K, B H = 16: 498 -> 589 TFLOP/s).  From two tiles per
+    // CU, and at d = 128 at any size, the 8-wave shape is faster.
+    if (!a.k_e4m3 && a.causal && a.d == 64 && wide_blocks >= kCUs && wide_blocks < 2 * kCUs) return {4, 1};
     if ((!a.k_e4m3 || (FA355_FP8_16 && a.d == 128)) && wide_blocks >= kCUs) return {8, 1};
     // Too few 128-row tiles to give every CU one: two key groups per tile
     // halve the serial chain of key tiles (worth it from 4 key tiles on).

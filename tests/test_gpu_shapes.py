@@ -1,7 +1,8 @@
 """Parity at the boundaries where the forward changes launch shape.
 
 The host picks a workgroup geometry from the grid size:
-- 8 waves (256 query rows) once B*H*ceil(Nq/256) >= 256, 16-bit K only;
+- 8 waves (256 query rows) once B*H*ceil(Nq/256) >= 256, 16-bit K only, and
+  causal at d = 64 only from B*H*ceil(Nq/256) >= 512 (4 waves below that);
 - two 4-wave key groups on 128 rows once B*H*ceil(Nq/128) <= 256 and Nkv > 192,
   or, causal at d = 64 with 16-bit K, two 2-wave key groups on 64 rows;
 - 4 waves (128 rows) otherwise, and always for E4M3 K when the grid is large.
@@ -27,8 +28,11 @@ CASES = [
     # B, H, Nq, Nkv, d, causal, dtype    16-bit K shape / E4M3 K shape
     (1, 128, 512, 512, 128, True, "f16"),   # 8 waves: exactly 256 wide blocks / 4 waves
     (1, 255, 256, 256, 64, False, "bf16"),  # 4 waves: 255 wide blocks, 510 tiles / 4 waves
-    (1, 256, 128, 193, 64, True, "f16"),    # 8 waves: 256 wide blocks / key groups: 256 tiles, 193 keys
-    (1, 256, 128, 192, 64, True, "bf16"),   # 8 waves / 4 waves: 192 keys
+    (1, 256, 128, 193, 64, True, "f16"),    # 4 waves: 256 wide blocks, causal d = 64 / key groups: 256 tiles, 193 keys
+    (1, 256, 128, 192, 64, True, "bf16"),   # 4 waves: 256 wide blocks, causal d = 64 / 4 waves: 192 keys
+    (1, 256, 512, 512, 64, True, "f16"),    # 8 waves: 512 wide blocks, causal d = 64 / 4 waves
+    (1, 255, 512, 600, 64, True, "bf16"),   # 4 waves: 510 wide blocks, causal d = 64, Nq < Nkv (both)
+    (1, 256, 128, 193, 64, False, "f16"),   # 8 waves: 256 wide blocks, no mask / key groups
     (1, 128, 256, 193, 128, False, "bf16"),  # key groups: 256 tiles, 193 keys (both)
     (1, 128, 256, 192, 128, False, "f16"),  # 4 waves: 192 keys (both)
     (1, 129, 256, 400, 64, True, "bf16"),   # 4 waves: 258 tiles (both)
