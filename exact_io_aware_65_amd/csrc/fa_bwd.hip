@@ -19,8 +19,11 @@
 //   bwd_dq_kernel     query blocks outer (each wave owns 32 queries, Q and dO
 //                     in registers), key tiles streamed through LDS;
 //                     accumulates dQ^T += K^T dS^T.
-// Recomputing S and dP in both of the last two kernels costs 7 products
-// instead of 5, but no partial sums cross workgroups: no atomics, results are
+// The two passes come in two forms: bwd_dkdv16_kernel and bwd_dq16_kernel on
+// the 16x16x32 MFMA (d = 128, and d = 64 once the grid gives every CU two
+// workgroups), and the 32x32x16 kernels named above for the small d = 64
+// grids.  Recomputing S and dP in both passes costs 7 products instead of 5,
+// but no partial sums cross workgroups: no atomics, results are
 // deterministic.
 //
 // MFMA layouts (32x32x16, lane l holds column l % 32 of the accumulator):
@@ -565,7 +568,8 @@ void bwd_dq_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dQ on the 16x16x32 MFMA (d = 128): the forward's fragment layout.  Per wave
+// dQ on the 16x16x32 MFMA (d = 128, and d = 64 on wide grids): the forward's
+// fragment layout.  Per wave
 // 32 queries as two 16-query blocks qb; per 64-key tile
 //
 //   S^T  (16 keys x 16 queries) = K (16 keys x 32 dims) Q^T     (A: K rows)
@@ -842,8 +846,9 @@ void bwd_dq16_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV on the 16x16x32 MFMA (d = 128).  Per wave 32 keys as two 16-key
-// blocks kb; per 32-query sub-tile (two 16-query blocks qb)
+// dK, dV on the 16x16x32 MFMA (d = 128, and d = 64 on wide grids).  Per wave
+// 32 keys as two 16-key blocks kb; per 32-query sub-tile (two 16-query blocks
+// qb)
 //
 //   S   (16 queries x 16 keys) = Q (16 queries x 32 dims) K^T    (A: Q rows)
 //   dP  (16 queries x 16 keys) = dO (16 queries x 32 dims) V^T   (A: dO rows)
