@@ -569,8 +569,8 @@ void bwd_dq_kernel(BwdParams p)
 
 // ---------------------------------------------------------------------------
 // dQ on the 16x16x32 MFMA (d = 128, and d = 64 on wide grids): the forward's
-// fragment layout.  Per wave
-// 32 queries as two 16-query blocks qb; per 64-key tile
+// fragment layout.  Per wave 32 queries as two 16-query blocks qb; per 64-key
+// tile
 //
 //   S^T  (16 keys x 16 queries) = K (16 keys x 32 dims) Q^T     (A: K rows)
 //   dP^T (16 keys x 16 queries) = V (16 keys x 32 dims) dO^T    (A: V rows)
