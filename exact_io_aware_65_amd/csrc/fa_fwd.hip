@@ -90,10 +90,11 @@ __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1)
 // b128 group of 16 lanes (lanes {0-3, 12-15, 20-27} and the like, see the
 // file comment) holds rows swap23 of those lanes, i.e. rows {0-3, 12-15,
 // 20-27} mod 32, whose low four bits are all distinct: the permutation must
-// send those 16 rows to 16 distinct 16-byte bank groups.  V is read transposed: 32 lanes
-// cover 4 consecutive rows (starting at a multiple of 4) x 64 bytes, so the 4
-// rows must land in 4 distinct 64-byte bank segments.  For d = 64 two rows
-// share one 256-byte bank line, hence the extra shift by one row bit.
+// send those 16 rows to 16 distinct 16-byte bank groups.  V is read
+// transposed: 32 lanes cover 4 consecutive rows (starting at a multiple of 4)
+// x 64 bytes, so the 4 rows must land in 4 distinct 64-byte bank segments.
+// For d = 64 two rows share one 256-byte bank line, hence the extra shift by
+// one row bit.
 //
 // K rows are 2d bytes (16-bit K) or d bytes (E4M3 K): 256, 128 or 64 bytes,
 // i.e. one, a half or a quarter of a 256-byte bank line.  The 16 rows read
